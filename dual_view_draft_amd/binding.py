@@ -1,0 +1,248 @@
+"""Python binding of liborthrus (the C ABI in include/orthrus.h).
+
+Argument marshalling only: torch tensors supply device memory and the HIP
+stream, every computation runs in the library's HIP kernels.  Each function
+has the name of the C entry point it calls.  There is no fallback: if the
+library is not built, or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liborthrus.so")
+_lib = None
+
+ORTHRUS_PAGE_SIZE = 16
+ORTHRUS_MAX_BLOCK = 64
+
+
+class OrthrusError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load_library()
+        name = lib.orthrus_status_string(status).decode()
+        detail = lib.orthrus_last_error().decode()
+        super().__init__(f"{where}: {name} ({status}): {detail}")
+        self.status = status
+
+
+class orthrus_kv(ctypes.Structure):
+    _fields_ = [("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32)]
+
+
+EXPORTS = {
+    # name: (restype, argtypes)
+    "orthrus_abi_version": (ctypes.c_int, []),
+    "orthrus_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "orthrus_last_error": (ctypes.c_char_p, []),
+    "orthrus_attn_split_tokens": (ctypes.c_int, [ctypes.c_int] * 3),
+    "orthrus_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 7),
+    "orthrus_attn_draft": (ctypes.c_int, [ctypes.POINTER(orthrus_kv)] + [ctypes.c_void_p] * 4 +
+                           [ctypes.c_int] * 3 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "orthrus_attn_verify": None,  # same signature as orthrus_attn_draft
+    "orthrus_argmax_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 2),
+    "orthrus_argmax": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "orthrus_accept": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 3 +
+                       [ctypes.c_void_p] * 4 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "orthrus_commit_kv": (ctypes.c_int, [ctypes.POINTER(orthrus_kv), ctypes.c_int, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p]),
+}
+EXPORTS["orthrus_attn_verify"] = EXPORTS["orthrus_attn_draft"]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load liborthrus.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(python -m dual_view_draft_amd.build)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise OrthrusError(rc, where)
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+@dataclasses.dataclass
+class PagedKV:
+    """One layer's view of the shared paged cache (tensors, device memory).
+
+    k_pages, v_pages: bf16 [num_pages, Hkv, 16, D]; block_table: int32
+    [B, max_pages]; seq_lens: int32 [B]."""
+    k_pages: torch.Tensor
+    v_pages: torch.Tensor
+    block_table: torch.Tensor
+    seq_lens: torch.Tensor
+
+    def c_struct(self) -> orthrus_kv:
+        for t, dt in ((self.k_pages, torch.bfloat16), (self.v_pages, torch.bfloat16),
+                      (self.block_table, torch.int32), (self.seq_lens, torch.int32)):
+            if t.dtype != dt:
+                raise ValueError(f"expected {dt}, got {t.dtype}")
+        n, hkv, p, d = self.k_pages.shape
+        if tuple(self.v_pages.shape) != (n, hkv, p, d):
+            raise ValueError("k_pages and v_pages shapes differ")
+        return orthrus_kv(_ptr(self.k_pages), _ptr(self.v_pages), _ptr(self.block_table),
+                          _ptr(self.seq_lens), n, p, hkv, d, self.block_table.shape[1])
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.k_pages.shape[3])
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.k_pages.shape[1])
+
+
+# ---------------------------------------------------------------------------
+def orthrus_abi_version() -> int:
+    return load_library().orthrus_abi_version()
+
+
+def orthrus_status_string(status: int) -> str:
+    return load_library().orthrus_status_string(status).decode()
+
+
+def orthrus_last_error() -> str:
+    return load_library().orthrus_last_error().decode()
+
+
+def orthrus_attn_split_tokens(batch: int, num_kv_heads: int, max_ctx: int) -> int:
+    return load_library().orthrus_attn_split_tokens(batch, num_kv_heads, max_ctx)
+
+
+def orthrus_attn_workspace_bytes(batch, block_k, num_q_heads, num_kv_heads, head_dim, max_ctx,
+                                 split_tokens=0) -> int:
+    return load_library().orthrus_attn_workspace_bytes(batch, block_k, num_q_heads, num_kv_heads,
+                                                       head_dim, max_ctx, split_tokens)
+
+
+def attn_workspace(kv: PagedKV, q: torch.Tensor, max_ctx: int, split_tokens: int = 0) -> torch.Tensor:
+    B, K, Hq, D = q.shape
+    n = orthrus_attn_workspace_bytes(B, K, Hq, kv.num_kv_heads, D, max_ctx, split_tokens)
+    if n == 0:
+        raise ValueError("unsupported attention shape")
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def _attention(fn_name, kv, q, k_blk, v_blk, out, max_ctx, scale, split_tokens, workspace, stream):
+    B, K, Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = attn_workspace(kv, q, max_ctx, split_tokens)
+    kvs = kv.c_struct()
+    rc = getattr(load_library(), fn_name)(
+        ctypes.byref(kvs), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(out), B, K, Hq,
+        float(scale), int(max_ctx), int(split_tokens), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, fn_name)
+    return out
+
+
+def orthrus_attn_draft(kv: PagedKV, q, k_blk, v_blk, out, *, max_ctx: int, scale=None,
+                       split_tokens: int = 0, workspace=None, stream=None):
+    """Draft pass (diffusion view): every block row sees the cache and the whole block."""
+    return _attention("orthrus_attn_draft", kv, q, k_blk, v_blk, out, max_ctx, scale,
+                      split_tokens, workspace, stream)
+
+
+def orthrus_attn_verify(kv: PagedKV, q, k_blk, v_blk, out, *, max_ctx: int, scale=None,
+                        split_tokens: int = 0, workspace=None, stream=None):
+    """Verify pass (AR view): block row i sees the cache and block rows 0..i."""
+    return _attention("orthrus_attn_verify", kv, q, k_blk, v_blk, out, max_ctx, scale,
+                      split_tokens, workspace, stream)
+
+
+def orthrus_argmax_workspace_bytes(rows: int, vocab: int) -> int:
+    return load_library().orthrus_argmax_workspace_bytes(rows, vocab)
+
+
+def argmax_workspace(rows: int, vocab: int, device) -> torch.Tensor:
+    return torch.empty(orthrus_argmax_workspace_bytes(rows, vocab), dtype=torch.uint8, device=device)
+
+
+def orthrus_argmax(logits: torch.Tensor, out: torch.Tensor, *, workspace=None, stream=None):
+    """out[r] = lowest index of the maximum of logits[r] (logits fp32 [..., V])."""
+    if logits.dtype != torch.float32 or out.dtype != torch.int32:
+        raise ValueError("logits must be float32 and out int32")
+    V = logits.shape[-1]
+    rows = logits.numel() // V
+    if workspace is None:
+        workspace = argmax_workspace(rows, V, logits.device)
+    rc = load_library().orthrus_argmax(_ptr(logits), rows, V, _ptr(out), _ptr(workspace),
+                                       workspace.numel(), _stream(stream))
+    _check(rc, "orthrus_argmax")
+    return out
+
+
+def orthrus_accept(logits_a: torch.Tensor, draft: torch.Tensor, ar_tokens, n_acc, n_emit,
+                   next_anchor, *, workspace=None, stream=None):
+    """Consensus: AR argmax of logits_a [B,K,V] and the longest prefix where draft matches."""
+    if logits_a.dtype != torch.float32:
+        raise ValueError("logits_a must be float32")
+    for t in (draft, ar_tokens, n_acc, n_emit, next_anchor):
+        if t.dtype != torch.int32:
+            raise ValueError("token and count tensors must be int32")
+    B, K, V = logits_a.shape
+    if workspace is None:
+        workspace = argmax_workspace(B * K, V, logits_a.device)
+    rc = load_library().orthrus_accept(_ptr(logits_a), _ptr(draft), B, K, V, _ptr(ar_tokens),
+                                       _ptr(n_acc), _ptr(n_emit), _ptr(next_anchor),
+                                       _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "orthrus_accept")
+
+
+def orthrus_commit_kv(kv_layer0: PagedKV, k_blk: torch.Tensor, v_blk: torch.Tensor,
+                      n_emit: torch.Tensor, seq_lens_out: torch.Tensor, *,
+                      pool_layer_stride: int = 0, stream=None):
+    """Append the accepted rows' K/V (k_blk, v_blk: bf16 [layers,B,K,Hkv,D]) to the cache.
+
+    kv_layer0 describes layer 0's pools; layer l's pools start pool_layer_stride
+    elements later (pass the stride of a [layers, num_pages, Hkv, 16, D] pool)."""
+    layers, B, K = k_blk.shape[:3]
+    kvs = kv_layer0.c_struct()
+    blk_stride = k_blk.stride(0) if layers > 1 else 0
+    rc = load_library().orthrus_commit_kv(ctypes.byref(kvs), layers, int(pool_layer_stride),
+                                          _ptr(k_blk), _ptr(v_blk), int(blk_stride), _ptr(n_emit),
+                                          B, K, _ptr(seq_lens_out), _stream(stream))
+    _check(rc, "orthrus_commit_kv")

@@ -1,0 +1,177 @@
+// Host-side argument checking and launch planning (see check.h).
+#include "check.h"
+
+#include <cmath>
+#include <cstdio>
+
+namespace orthrus {
+namespace {
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int fail(std::string* err, int code, const char* msg) {
+  if (err) *err = msg;
+  return code;
+}
+
+int check_kv(const orthrus_kv* kv, std::string* err) {
+  if (!kv) return fail(err, ORTHRUS_ERR_INVALID_ARG, "kv descriptor is null");
+  if (!kv->k_pages || !kv->v_pages || !kv->block_table || !kv->seq_lens)
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "kv: null k_pages/v_pages/block_table/seq_lens");
+  if (!aligned16(kv->k_pages) || !aligned16(kv->v_pages))
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "kv: page pools must be 16-byte aligned");
+  if (kv->page_size != ORTHRUS_PAGE_SIZE)
+    return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "kv: page_size must be 16");
+  if (kv->head_dim != 64 && kv->head_dim != 128)
+    return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "kv: head_dim must be 64 or 128");
+  if (kv->num_kv_heads < 1 || kv->num_pages < 1 || kv->max_pages_per_seq < 1)
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "kv: num_kv_heads, num_pages, max_pages_per_seq must be >= 1");
+  return ORTHRUS_OK;
+}
+
+}  // namespace
+
+const char* status_string(int status) {
+  switch (status) {
+    case ORTHRUS_OK: return "ORTHRUS_OK";
+    case ORTHRUS_ERR_INVALID_ARG: return "ORTHRUS_ERR_INVALID_ARG";
+    case ORTHRUS_ERR_UNSUPPORTED_SHAPE: return "ORTHRUS_ERR_UNSUPPORTED_SHAPE";
+    case ORTHRUS_ERR_WORKSPACE_TOO_SMALL: return "ORTHRUS_ERR_WORKSPACE_TOO_SMALL";
+    case ORTHRUS_ERR_CAPACITY: return "ORTHRUS_ERR_CAPACITY";
+    case ORTHRUS_ERR_HIP: return "ORTHRUS_ERR_HIP";
+    default: return "ORTHRUS_ERR_UNKNOWN";
+  }
+}
+
+int attn_split_tokens(int B, int Hkv, int max_ctx) {
+  if (B < 1 || Hkv < 1 || max_ctx < 0) return kTile * 4;
+  // Aim for about two workgroups per compute unit (256 CUs) when every
+  // sequence is max_ctx long; splits stay between 4 and 64 tiles long.
+  const int64_t work = int64_t(B) * Hkv * (int64_t(max_ctx) + kTile);
+  int64_t s = round_up(ceil_div(work, 512), kTile);
+  if (s < 4 * kTile) s = 4 * kTile;
+  if (s > 64 * kTile) s = 64 * kTile;
+  return int(s);
+}
+
+bool plan_attention_shape(int B, int K, int Hq, int Hkv, int D, int max_ctx, int split_tokens,
+                          AttnPlan* p, std::string* why) {
+  auto no = [&](const char* m) { if (why) *why = m; return false; };
+  if (B < 0) return no("batch must be >= 0");
+  if (K < 1 || K > ORTHRUS_MAX_BLOCK) return no("block_k must be in [1, 64]");
+  if (Hkv < 1 || Hq < 1 || Hq % Hkv) return no("num_q_heads must be a positive multiple of num_kv_heads");
+  if (Hq / Hkv > kMaxGroup) return no("group size num_q_heads/num_kv_heads must be <= 16");
+  if (D != 64 && D != 128) return no("head_dim must be 64 or 128");
+  if (max_ctx < 0 || max_ctx > (1 << 30)) return no("max_ctx out of range");
+  if (split_tokens < 0 || split_tokens % kTile) return no("split_tokens must be 0 or a positive multiple of 64");
+  p->B = B; p->K = K; p->Hq = Hq; p->Hkv = Hkv; p->G = Hq / Hkv; p->D = D;
+  p->max_ctx = max_ctx;
+  p->split = split_tokens ? split_tokens : attn_split_tokens(B, Hkv, max_ctx);
+  p->nsplit = int(ceil_div(int64_t(max_ctx) + K, p->split));
+  p->rows = p->G * K;
+  p->nchunks = int(ceil_div(p->rows, kMaxRowsPerCta));
+  p->rows_per_chunk = p->rows > kMaxRowsPerCta ? kMaxRowsPerCta : int(round_up(p->rows, kRowsPerWave));
+  const int64_t parts = int64_t(B) * Hkv * p->nchunks * p->nsplit * p->rows_per_chunk;
+  p->part_o_bytes = size_t(round_up(parts * D * 4, 256));
+  p->part_ml_bytes = size_t(round_up(parts * 2 * 4, 256));
+  p->ws_bytes = p->part_o_bytes + p->part_ml_bytes;
+  return true;
+}
+
+int check_attention(const orthrus_kv* kv, const void* q, const void* k_blk, const void* v_blk,
+                    const void* out, int B, int K, int Hq, float scale, int max_ctx,
+                    int split_tokens, const void* ws, size_t ws_bytes, AttnPlan* plan,
+                    std::string* err) {
+  int rc = check_kv(kv, err);
+  if (rc) return rc;
+  std::string why;
+  if (!plan_attention_shape(B, K, Hq, kv->num_kv_heads, kv->head_dim, max_ctx, split_tokens, plan, &why)) {
+    if (err) *err = why;
+    return (B < 0 || max_ctx < 0 || split_tokens < 0 || split_tokens % kTile)
+               ? ORTHRUS_ERR_INVALID_ARG : ORTHRUS_ERR_UNSUPPORTED_SHAPE;
+  }
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (int64_t(kv->max_pages_per_seq) * ORTHRUS_PAGE_SIZE < int64_t(max_ctx) + K)
+    return fail(err, ORTHRUS_ERR_CAPACITY, "block table shorter than max_ctx + block_k positions");
+  if (B == 0) return ORTHRUS_OK;
+  if (!q || !k_blk || !v_blk || !out)
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "null q/k_blk/v_blk/out");
+  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(out))
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "q/k_blk/v_blk/out must be 16-byte aligned");
+  if (!ws || !aligned16(ws)) return fail(err, ORTHRUS_ERR_INVALID_ARG, "workspace null or misaligned");
+  if (ws_bytes < plan->ws_bytes)
+    return fail(err, ORTHRUS_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than orthrus_attn_workspace_bytes()");
+  return ORTHRUS_OK;
+}
+
+bool plan_argmax(int rows, int V, ArgmaxPlan* p) {
+  if (rows < 0 || V < 1) return false;
+  p->rows = rows;
+  p->V = V;
+  // about 2048 workgroups over the whole matrix, each at least 4096 values
+  int64_t chunk = round_up(ceil_div(int64_t(V) * (rows > 0 ? rows : 1), 2048), 1024);
+  if (chunk < 4096) chunk = 4096;
+  if (chunk > V) chunk = round_up(V, 4);
+  p->chunk = int(chunk);
+  p->nchunks = int(ceil_div(V, chunk));
+  p->ws_bytes = size_t(round_up(int64_t(rows > 0 ? rows : 1) * p->nchunks * 8, 256));
+  return true;
+}
+
+int check_argmax(const float* logits, int rows, int V, const int32_t* out, const void* ws,
+                 size_t ws_bytes, ArgmaxPlan* plan, std::string* err) {
+  if (rows < 0 || V < 1) return fail(err, ORTHRUS_ERR_INVALID_ARG, "rows must be >= 0 and vocab >= 1");
+  if (rows > 65535) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "at most 65535 rows per call");
+  plan_argmax(rows, V, plan);
+  if (rows == 0) return ORTHRUS_OK;
+  if (!logits || !out) return fail(err, ORTHRUS_ERR_INVALID_ARG, "null logits/out");
+  if (!ws || !aligned16(ws)) return fail(err, ORTHRUS_ERR_INVALID_ARG, "workspace null or misaligned");
+  if (ws_bytes < plan->ws_bytes)
+    return fail(err, ORTHRUS_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than orthrus_argmax_workspace_bytes()");
+  return ORTHRUS_OK;
+}
+
+int check_accept(const float* logits_a, const int32_t* draft, int B, int K, int V,
+                 const int32_t* a, const int32_t* n_acc, const int32_t* n_emit,
+                 const int32_t* next_anchor, const void* ws, size_t ws_bytes, ArgmaxPlan* plan,
+                 std::string* err) {
+  if (B < 0) return fail(err, ORTHRUS_ERR_INVALID_ARG, "batch must be >= 0");
+  if (K < 1 || K > ORTHRUS_MAX_BLOCK) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "block_k must be in [1, 64]");
+  if (V < 1) return fail(err, ORTHRUS_ERR_INVALID_ARG, "vocab must be >= 1");
+  if (int64_t(B) * K > (int64_t(1) << 30)) return fail(err, ORTHRUS_ERR_INVALID_ARG, "batch * block_k too large");
+  int rc = check_argmax(logits_a, B * K, V, a, ws, ws_bytes, plan, err);
+  if (rc) return rc;
+  if (B == 0) return ORTHRUS_OK;
+  if (!draft || !n_acc || !n_emit || !next_anchor)
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "null draft/n_acc/n_emit/next_anchor");
+  return ORTHRUS_OK;
+}
+
+int check_commit(const orthrus_kv* kv, int layers, int64_t pool_layer_stride, const void* k_blk,
+                 const void* v_blk, int64_t blk_layer_stride, const int32_t* n_emit, int B, int K,
+                 const int32_t* seq_lens_out, std::string* err) {
+  int rc = check_kv(kv, err);
+  if (rc) return rc;
+  if (layers < 1) return fail(err, ORTHRUS_ERR_INVALID_ARG, "num_layers must be >= 1");
+  if (B < 0) return fail(err, ORTHRUS_ERR_INVALID_ARG, "batch must be >= 0");
+  if (K < 1 || K > ORTHRUS_MAX_BLOCK) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "block_k must be in [1, 64]");
+  const int64_t pool_elems = int64_t(kv->num_pages) * kv->num_kv_heads * ORTHRUS_PAGE_SIZE * kv->head_dim;
+  const int64_t blk_elems = int64_t(B) * K * kv->num_kv_heads * kv->head_dim;
+  if (layers > 1 && (pool_layer_stride < pool_elems || blk_layer_stride < blk_elems))
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "layer strides smaller than one layer");
+  if (layers > 1 && ((pool_layer_stride * 2) % 16 || (blk_layer_stride * 2) % 16))
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "layer strides must keep 16-byte alignment");
+  if (B == 0) return ORTHRUS_OK;
+  if (!k_blk || !v_blk || !n_emit || !seq_lens_out)
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "null k_blk/v_blk/n_emit/seq_lens_out");
+  if (!aligned16(k_blk) || !aligned16(v_blk))
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "k_blk/v_blk must be 16-byte aligned");
+  if (seq_lens_out == kv->seq_lens)
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "seq_lens_out must not alias kv->seq_lens");
+  return ORTHRUS_OK;
+}
+
+}  // namespace orthrus

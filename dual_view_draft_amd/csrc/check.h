@@ -1,0 +1,64 @@
+// Host-side argument checking and launch planning for the Orthrus C ABI.
+// Pure C++ (no HIP headers): it is compiled into the library and, separately,
+// into a host-only test driver built with sanitizers.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/orthrus.h"
+
+namespace orthrus {
+
+constexpr int kTile = 64;          // tokens per attention tile (4 pages)
+constexpr int kRowsPerWave = 32;   // query rows per wavefront (one 32x32 MFMA block)
+constexpr int kMaxRowsPerCta = 128;
+constexpr int kMaxGroup = 16;
+
+// Geometry of one attention call, all derived on the host.
+struct AttnPlan {
+  int B = 0, K = 0, Hq = 0, Hkv = 0, G = 0, D = 0;
+  int max_ctx = 0;
+  int split = 0;           // tokens per context split (multiple of kTile)
+  int nsplit = 0;          // splits covering max_ctx + K positions
+  int rows = 0;            // G*K query rows per KV head
+  int nchunks = 0;         // row chunks of <= 128 rows
+  int rows_per_chunk = 0;  // multiple of 32
+  size_t part_o_bytes = 0, part_ml_bytes = 0, ws_bytes = 0;
+};
+
+struct ArgmaxPlan {
+  int rows = 0, V = 0, chunk = 0, nchunks = 0;
+  size_t ws_bytes = 0;
+};
+
+int attn_split_tokens(int B, int Hkv, int max_ctx);
+
+// Shape-only planning (no pointers); false if the shape is unsupported.
+bool plan_attention_shape(int B, int K, int Hq, int Hkv, int D, int max_ctx, int split_tokens,
+                          AttnPlan* plan, std::string* why);
+
+// Full check of an attention call; returns an orthrus_status.
+int check_attention(const orthrus_kv* kv, const void* q, const void* k_blk, const void* v_blk,
+                    const void* out, int B, int K, int Hq, float scale, int max_ctx,
+                    int split_tokens, const void* ws, size_t ws_bytes, AttnPlan* plan,
+                    std::string* err);
+
+bool plan_argmax(int rows, int V, ArgmaxPlan* plan);
+
+int check_argmax(const float* logits, int rows, int V, const int32_t* out, const void* ws,
+                 size_t ws_bytes, ArgmaxPlan* plan, std::string* err);
+
+int check_accept(const float* logits_a, const int32_t* draft, int B, int K, int V,
+                 const int32_t* a, const int32_t* n_acc, const int32_t* n_emit,
+                 const int32_t* next_anchor, const void* ws, size_t ws_bytes, ArgmaxPlan* plan,
+                 std::string* err);
+
+int check_commit(const orthrus_kv* kv, int layers, int64_t pool_layer_stride, const void* k_blk,
+                 const void* v_blk, int64_t blk_layer_stride, const int32_t* n_emit, int B, int K,
+                 const int32_t* seq_lens_out, std::string* err);
+
+const char* status_string(int status);
+
+}  // namespace orthrus

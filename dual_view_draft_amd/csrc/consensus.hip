@@ -1,0 +1,171 @@
+// Consensus of the two views: vocabulary argmax and longest matching prefix.
+//
+// The drafted tokens are the argmax of the diffusion view's logits; the AR
+// view's greedy tokens are the argmax of the verify pass's logits; drafted
+// tokens are accepted left to right while they equal the AR tokens, and the
+// AR token at the first mismatch is appended (gist.science technical summary
+// of "Orthrus: Memory-Efficient Parallel Token Generation via Dual-View
+// Diffusion", section 2.3 steps 1 and 3; Hacker News thread "Orthrus-Qwen3:
+// up to 7.8x tokens/forward ...", post #21).
+//
+// Argmax is an HBM stream over fp32 logits.  Every row is cut into chunks
+// processed by independent workgroups; each reduces its chunk to one 64-bit
+// key (order-preserving image of the value in the high word, bit-inverted
+// index in the low word).  The maximum key is the maximum value with the
+// lowest index, whatever order the reduction runs in, so the result is
+// deterministic and independent of the launch shape.  A small second kernel
+// reduces the chunk keys of each row (argmax) or of each sequence's K rows
+// and runs the prefix scan with one wavefront ballot (accept).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "check.h"
+#include "launch.h"
+
+namespace orthrus {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct PartialArgs {
+  const float* logits;  // [rows][V]
+  unsigned long long* keys;  // [rows][nchunks]
+  int rows, V, chunk, nchunks;
+};
+
+struct FinalArgs {
+  const unsigned long long* keys;
+  int32_t* out;
+  int rows, nchunks;
+};
+
+struct AcceptArgs {
+  const unsigned long long* keys;  // [B*K][nchunks]
+  const int32_t* draft;            // [B][K]
+  int32_t* a;
+  int32_t* n_acc;
+  int32_t* n_emit;
+  int32_t* next_anchor;
+  int B, K, nchunks;
+};
+
+// Monotone map float -> uint32 (-0.0 and +0.0 map to the same key).
+__device__ __forceinline__ uint32_t ordered_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ unsigned long long make_key(float x, int idx) {
+  return (static_cast<unsigned long long>(ordered_bits(x)) << 32) |
+         static_cast<unsigned long long>(~static_cast<uint32_t>(idx));
+}
+
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+
+__device__ __forceinline__ unsigned long long wave_max(unsigned long long k) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(k), off);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(k >> 32), off);
+    k = umax64(k, (static_cast<unsigned long long>(hi) << 32) | lo);
+  }
+  return k;
+}
+
+__device__ __forceinline__ int32_t key_index(unsigned long long k) {
+  return static_cast<int32_t>(~static_cast<uint32_t>(k));
+}
+
+__global__ __launch_bounds__(256) void argmax_partial_kernel(PartialArgs a) {
+  __shared__ unsigned long long red[4];
+  const int row = blockIdx.y;
+  const int c = blockIdx.x;
+  const int lo = c * a.chunk;
+  const int hi = min(lo + a.chunk, a.V);
+  const float* base = a.logits + size_t(row) * a.V;
+  unsigned long long best = 0ull;
+  if ((a.V & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0) {
+    const f32x4* b4 = reinterpret_cast<const f32x4*>(base);
+    for (int v4 = (lo >> 2) + threadIdx.x; v4 < (hi >> 2); v4 += 256) {
+      const f32x4 x = b4[v4];
+      const int v = v4 * 4;
+      best = umax64(best, make_key(x[0], v));
+      best = umax64(best, make_key(x[1], v + 1));
+      best = umax64(best, make_key(x[2], v + 2));
+      best = umax64(best, make_key(x[3], v + 3));
+    }
+  } else {
+    for (int v = lo + threadIdx.x; v < hi; v += 256) best = umax64(best, make_key(base[v], v));
+  }
+  best = wave_max(best);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    best = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
+    a.keys[size_t(row) * a.nchunks + c] = best;
+  }
+}
+
+__global__ __launch_bounds__(256) void argmax_final_kernel(FinalArgs a) {
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  if (row >= a.rows) return;
+  unsigned long long best = 0ull;
+  for (int c = 0; c < a.nchunks; ++c) best = umax64(best, a.keys[size_t(row) * a.nchunks + c]);
+  a.out[row] = key_index(best);
+}
+
+// One wavefront per sequence; lane i owns block row i (K <= 64).
+__global__ __launch_bounds__(64) void accept_kernel(AcceptArgs a) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  int32_t tok = 0;
+  bool mismatch = false;
+  if (i < a.K) {
+    const size_t row = size_t(b) * a.K + i;
+    unsigned long long best = 0ull;
+    for (int c = 0; c < a.nchunks; ++c) best = umax64(best, a.keys[row * a.nchunks + c]);
+    tok = key_index(best);
+    a.a[row] = tok;
+    mismatch = a.draft[row] != tok;
+  }
+  const unsigned long long bad = __ballot(mismatch);
+  const int n_acc = bad ? (__ffsll(static_cast<long long>(bad)) - 1) : a.K;
+  const int n_emit = n_acc < a.K ? n_acc + 1 : a.K;
+  const int32_t nxt = __shfl(tok, n_emit - 1);
+  if (i == 0) {
+    a.n_acc[b] = n_acc;
+    a.n_emit[b] = n_emit;
+    a.next_anchor[b] = nxt;
+  }
+}
+
+hipError_t launch_partial(const ArgmaxPlan& p, const float* logits, void* ws, hipStream_t stream) {
+  PartialArgs a{logits, static_cast<unsigned long long*>(ws), p.rows, p.V, p.chunk, p.nchunks};
+  return launch_kernel(&argmax_partial_kernel, dim3(p.nchunks, p.rows), dim3(256), stream, a);
+}
+
+}  // namespace
+
+hipError_t launch_argmax(const ArgmaxPlan& p, const float* logits, int32_t* out, void* ws,
+                         hipStream_t stream) {
+  hipError_t e = launch_partial(p, logits, ws, stream);
+  if (e != hipSuccess) return e;
+  FinalArgs f{static_cast<const unsigned long long*>(ws), out, p.rows, p.nchunks};
+  return launch_kernel(&argmax_final_kernel, dim3((p.rows + 255) / 256), dim3(256), stream, f);
+}
+
+hipError_t launch_accept(const ArgmaxPlan& p, const float* logits_a, const int32_t* draft, int B,
+                         int K, int32_t* a, int32_t* n_acc, int32_t* n_emit, int32_t* next_anchor,
+                         void* ws, hipStream_t stream) {
+  hipError_t e = launch_partial(p, logits_a, ws, stream);
+  if (e != hipSuccess) return e;
+  AcceptArgs x{static_cast<const unsigned long long*>(ws), draft, a, n_acc, n_emit, next_anchor,
+               B, K, p.nchunks};
+  return launch_kernel(&accept_kernel, dim3(B), dim3(64), stream, x);
+}
+
+}  // namespace orthrus

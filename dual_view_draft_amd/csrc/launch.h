@@ -1,0 +1,37 @@
+// Internal launch interface between the C ABI (abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "check.h"
+
+namespace orthrus {
+
+// Launch a kernel whose only parameter is an argument struct; returns the
+// launch status directly (hipLaunchKernel reports configuration errors itself,
+// so no sticky error of an unrelated earlier call is picked up).
+template <typename A>
+hipError_t launch_kernel(void (*kernel)(A), dim3 grid, dim3 block, hipStream_t stream, A args) {
+  void* ptrs[] = {static_cast<void*>(&args)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, stream);
+}
+
+hipError_t launch_attention(const AttnPlan& plan, const orthrus_kv& kv, const void* q,
+                            const void* k_blk, const void* v_blk, void* out, float scale,
+                            bool verify, void* ws, hipStream_t stream);
+
+hipError_t launch_argmax(const ArgmaxPlan& plan, const float* logits, int32_t* out, void* ws,
+                         hipStream_t stream);
+
+hipError_t launch_accept(const ArgmaxPlan& plan, const float* logits_a, const int32_t* draft,
+                         int B, int K, int32_t* a, int32_t* n_acc, int32_t* n_emit,
+                         int32_t* next_anchor, void* ws, hipStream_t stream);
+
+hipError_t launch_commit(const orthrus_kv& kv, int layers, int64_t pool_layer_stride,
+                         const void* k_blk, const void* v_blk, int64_t blk_layer_stride,
+                         const int32_t* n_emit, int B, int K, int32_t* seq_lens_out,
+                         hipStream_t stream);
+
+}  // namespace orthrus

@@ -1,0 +1,129 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the
+header declares, and rejects invalid arguments before any GPU work (host
+checks only; no kernel is launched here)."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "orthrus.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"ORTHRUS_API\s+[\w\s\*]+?\b(orthrus_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import dual_view_draft_amd as dv
+    return dv.load_library()
+
+
+def test_header_declares_the_method_entry_points():
+    names = declared_functions()
+    for n in ("orthrus_attn_draft", "orthrus_attn_verify", "orthrus_accept", "orthrus_commit_kv",
+              "orthrus_argmax"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (orthrus_\w+)", out))
+    assert set(declared_functions()) == exported
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def test_binding_covers_every_export():
+    import dual_view_draft_amd.binding as b
+    assert set(b.EXPORTS) == set(declared_functions())
+    for n in declared_functions():
+        assert callable(getattr(b, n))
+
+
+def test_version_and_status_strings(lib):
+    assert lib.orthrus_abi_version() == 1
+    assert lib.orthrus_status_string(-3) == b"ORTHRUS_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.orthrus_status_string(0) == b"ORTHRUS_OK"
+
+
+def test_workspace_queries(lib):
+    n = lib.orthrus_attn_workspace_bytes(1, 32, 32, 8, 128, 40960, 0)
+    split = lib.orthrus_attn_split_tokens(1, 8, 40960)
+    assert split % 64 == 0 and split > 0
+    nsplit = -(-(40960 + 32) // split)
+    assert n >= nsplit * 8 * 128 * (128 + 2) * 4
+    assert lib.orthrus_attn_workspace_bytes(1, 65, 32, 8, 128, 100, 0) == 0
+    assert lib.orthrus_attn_workspace_bytes(1, 32, 32, 8, 96, 100, 0) == 0
+    assert lib.orthrus_argmax_workspace_bytes(32, 151936) >= 32 * 8
+
+
+def _kv(b, **kw):
+    f = dict(k_pages=0x10000, v_pages=0x10000, block_table=0x20000, seq_lens=0x20000,
+             num_pages=4096, page_size=16, num_kv_heads=8, head_dim=128, max_pages_per_seq=2600)
+    f.update(kw)
+    return b.orthrus_kv(**f)
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(page_size=8), -2), (dict(head_dim=80), -2), (dict(k_pages=0), -1),
+    (dict(max_pages_per_seq=10), -4), (dict(v_pages=0x10004), -1),
+])
+def test_attention_rejects_bad_cache_descriptor(lib, change, status):
+    import dual_view_draft_amd.binding as b
+    kv = _kv(b, **change)
+    P = ctypes.c_void_p(0x10000)
+    for fn in (lib.orthrus_attn_draft, lib.orthrus_attn_verify):
+        rc = fn(ctypes.byref(kv), P, P, P, P, 1, 32, 32, 0.088, 1000, 0, P, 1 << 40, None)
+        assert rc == status, lib.orthrus_last_error()
+        assert lib.orthrus_last_error() != b""
+
+
+def test_attention_rejects_small_workspace_before_any_launch(lib):
+    import dual_view_draft_amd.binding as b
+    kv = _kv(b)
+    P = ctypes.c_void_p(0x10000)
+    need = lib.orthrus_attn_workspace_bytes(1, 32, 32, 8, 128, 1000, 0)
+    rc = lib.orthrus_attn_verify(ctypes.byref(kv), P, P, P, P, 1, 32, 32, 0.088, 1000, 0, P, need - 16, None)
+    assert rc == -3 and b"workspace" in lib.orthrus_last_error()
+
+
+def test_batch_zero_calls_succeed_without_gpu(lib):
+    import dual_view_draft_amd.binding as b
+    kv = _kv(b)
+    assert lib.orthrus_attn_draft(ctypes.byref(kv), None, None, None, None, 0, 32, 32, 0.088, 1000,
+                                  0, None, 0, None) == 0
+    assert lib.orthrus_argmax(None, 0, 151936, None, None, 0, None) == 0
+    assert lib.orthrus_accept(None, None, 0, 32, 151936, None, None, None, None, None, 0, None) == 0
+    assert lib.orthrus_commit_kv(ctypes.byref(kv), 1, 0, None, None, 0, None, 0, 32, None, None) == 0
+
+
+def test_consensus_and_commit_argument_checks(lib):
+    import dual_view_draft_amd.binding as b
+    P = ctypes.c_void_p(0x10000)
+    assert lib.orthrus_argmax(P, 4, 0, P, P, 1 << 20, None) == -1
+    assert lib.orthrus_argmax(P, 4, 1000, P, P, 8, None) == -3
+    assert lib.orthrus_accept(P, P, 1, 65, 1000, P, P, P, P, P, 1 << 20, None) == -2
+    kv = _kv(b)
+    assert lib.orthrus_commit_kv(ctypes.byref(kv), 1, 0, P, P, 0, P, 1, 32,
+                                 ctypes.c_void_p(0x20000), None) == -1   # aliases seq_lens
+    assert lib.orthrus_commit_kv(ctypes.byref(kv), 0, 0, P, P, 0, P, 1, 32, P, None) == -1
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_host_checks_under_sanitizers(tmp_path):
+    exe = str(tmp_path / "check_driver")
+    csrc = os.path.join(ROOT, "dual_view_draft_amd", "csrc")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", f"-I{csrc}", f"-I{os.path.join(ROOT, 'include')}",
+           os.path.join(ROOT, "tests", "host", "check_driver.cpp"), os.path.join(csrc, "check.cpp"),
+           "-o", exe]
+    subprocess.run(cmd, check=True, capture_output=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "OK (0 failures)" in r.stdout
