@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of one Orthrus decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+  draft attention (diffusion view, block-bidirectional mask)
+  -> draft argmax over the draft logits
+  -> verify attention (AR view, causal inside the block)
+  -> accept (AR argmax + longest matching prefix)
+  -> commit of the accepted rows' K/V into the paged cache.
+Everything runs in liborthrus (HIP, gfx950) on torch's current stream; inputs
+are resident in HBM before the timed region.  The KV pool is replicated into
+several independently permuted copies (more bytes than the 256 MB Infinity
+Cache) and the steps rotate through them, so repeated steps cannot be served
+from the last-level cache.
+
+Output: one JSON line (metric, value, roofline of the attention pass,
+cpu_baseline of the CPU oracle on the same workload, per-op timings).
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload qwen3_8b_40k]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+METRIC = "block-attn KV-read GB/s (% HBM peak) + draft/verify steps/s, 8B shape @40K"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_kernel_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "dual_view_draft_amd", "csrc", "attn.hip")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="qwen3_8b_40k",
+                   choices=["qwen3_8b_40k", "qwen3_8b_4k", "qwen3_8b_ragged16", "tiny"])
+    p.add_argument("--pools", type=int, default=0, help="KV pool copies to rotate (0 = auto)")
+    p.add_argument("--split", type=int, default=0, help="split_tokens override (0 = library choice)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-steps", type=int, default=3)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kv_bytes_per_launch: float):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, or None if the attention kernel changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("attn_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_split_launch")
+
+
+def setup(args, torch, dv, synth):
+    w = dict(synth.WORKLOADS[args.workload])
+    B, K, Hq, Hkv, D, V = w["B"], w["K"], w["Hq"], w["Hkv"], w["D"], w["V"]
+    lens = w["seq_lens"] if w["seq_lens"] is not None else synth.ragged_lengths(w["seed"], B)
+    case = synth.make_paged_case(w["seed"], B, K, Hq, Hkv, D, lens, fill="sentinel")
+    qv, kbv, vbv = synth.make_block_qkv(w["seed"] + 100, B, K, Hq, Hkv, D)
+    cons = synth.make_consensus_case(w["seed"], B, K, V, dist=w["accept"])
+    return w, case, (qv, kbv, vbv), cons
+
+
+def to_dev16(torch, np, a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dual_view_draft_amd as dv
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dv.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calibration:
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(5):
+            torch.add(a, 0.0, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": a.numel() * 4,
+                          "copy_calibration_bytes_written": b.numel() * 4}))
+        return
+
+    w, case, (qv, kbv, vbv), cons = setup(args, torch, dv, synth)
+    B, K, Hq, Hkv, D, V = w["B"], w["K"], w["Hq"], w["Hkv"], w["D"], w["V"]
+    L = [int(x) for x in case.seq_lens]
+    max_ctx = max(L)
+    kv_bytes = 4 * Hkv * D * sum(L)                       # K and V, bf16, every cached token
+    pool_bytes = 2 * case.k_pages[0].nbytes
+    n_pools = args.pools or max(2, min(16, math.ceil(1.3e9 / pool_bytes)))
+
+    # ---- device inputs --------------------------------------------------------
+    kp0 = to_dev16(torch, np, case.k_pages[0])
+    vp0 = to_dev16(torch, np, case.v_pages[0])
+    table0 = torch.from_numpy(case.block_table).to(dev)
+    seq_lens = torch.from_numpy(case.seq_lens).to(dev)
+    kvs = [dv.PagedKV(kp0, vp0, table0, seq_lens)]
+    g = torch.Generator(device="cpu").manual_seed(12345)
+    for _ in range(1, n_pools):
+        perm = torch.randperm(case.num_pages, generator=g).to(dev)
+        inv = torch.empty_like(perm)
+        inv[perm] = torch.arange(case.num_pages, device=dev)
+        kvs.append(dv.PagedKV(kp0[perm].contiguous(), vp0[perm].contiguous(),
+                              inv[table0.long()].to(torch.int32).contiguous(), seq_lens))
+    q_d, kb_d, vb_d = (to_dev16(torch, np, x) for x in (case.q, case.k_blk, case.v_blk))
+    q_v, kb_v, vb_v = (to_dev16(torch, np, x) for x in (qv, kbv, vbv))
+    logits_d = torch.from_numpy(cons.logits_d).to(dev)
+    logits_a = torch.from_numpy(cons.logits_a).to(dev)
+    out_d = torch.empty_like(q_d)
+    out_v = torch.empty_like(q_v)
+    d_tok = torch.empty((B, K), dtype=torch.int32, device=dev)
+    a_tok = torch.empty((B, K), dtype=torch.int32, device=dev)
+    n_acc, n_emit, nxt, lens_out = (torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4))
+    ws_attn = dv.attn_workspace(kvs[0], q_d, max_ctx, args.split)
+    ws_arg = dv.argmax_workspace(B * K, V, dev)
+    kb_commit, vb_commit = kb_v[None], vb_v[None]
+    torch.cuda.synchronize()
+
+    ops = ["draft_attn", "draft_argmax", "verify_attn", "accept", "commit"]
+
+    def step(i, ev=None):
+        kv = kvs[(2 * i) % n_pools]           # draft and verify read different pool copies,
+        kv_v = kvs[(2 * i + 1) % n_pools]     # as a real model's two passes are layers apart
+        if ev: ev[0].record(stream)
+        dv.orthrus_attn_draft(kv, q_d, kb_d, vb_d, out_d, max_ctx=max_ctx, split_tokens=args.split,
+                              workspace=ws_attn, stream=stream)
+        if ev: ev[1].record(stream)
+        dv.orthrus_argmax(logits_d, d_tok, workspace=ws_arg, stream=stream)
+        if ev: ev[2].record(stream)
+        dv.orthrus_attn_verify(kv_v, q_v, kb_v, vb_v, out_v, max_ctx=max_ctx, split_tokens=args.split,
+                               workspace=ws_attn, stream=stream)
+        if ev: ev[3].record(stream)
+        dv.orthrus_accept(logits_a, d_tok, a_tok, n_acc, n_emit, nxt, workspace=ws_arg, stream=stream)
+        if ev: ev[4].record(stream)
+        dv.orthrus_commit_kv(kv_v, kb_commit, vb_commit, n_emit, lens_out, stream=stream)
+        if ev: ev[5].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # sanity: the consensus reproduces the drawn accepted lengths
+    assert torch.equal(n_acc.cpu(), torch.from_numpy(cons.n_acc)), "accept mismatch"
+
+    # ---- timed region: plain steps, whole-job clock --------------------------
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # ---- per-op breakdown (separate pass, events between the calls) ----------
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    per_op = {op: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, op in enumerate(ops)}
+    op_ms = {op: statistics.mean(v) for op, v in per_op.items()}
+    op_med = {op: statistics.median(v) for op, v in per_op.items()}
+
+    # ---- algorithmic bytes / flops per attention launch ----------------------
+    pages_read = sum(-(-l // 16) for l in L)
+    attn_bytes = (kv_bytes + 2 * B * K * Hq * D * 2 + 2 * 2 * B * K * Hkv * D * 2 + 4 * pages_read + 4 * B)
+    attn_flops = 4.0 * Hq * K * D * sum(l + K for l in L)
+    dom = max(("draft_attn", "verify_attn"), key=lambda o: op_ms[o])
+    dom_s = op_ms[dom] * 1e-3
+    achieved = attn_bytes / dom_s / 1e9
+    traffic = measured_traffic(attn_bytes)
+
+    value = 2 * kv_bytes / (ms_per_step * 1e-3) / 1e9   # KV bytes of both passes per step
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1/sqrt(D)) bf16 Q/K/V, shuffled 16-token pages; "
+                "planted-argmax fp32 logits with geometric(0.15) accepted lengths)",
+        "config": {"workload": args.workload, "batch": B, "context": L if B > 1 else L[0],
+                   "block_k": K, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": 16,
+                   "vocab": V, "split_tokens": dv.orthrus_attn_split_tokens(B, Hkv, max_ctx)
+                   if args.split == 0 else args.split, "kv_pool_copies": n_pools},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "steps_per_s": round(1e3 / ms_per_step, 1),
+        "tokens_per_step_expected": round(float(sum(min(int(a) + 1, K) for a in cons.n_acc)), 2),
+        "op_ms_mean": {k: round(v, 4) for k, v in op_ms.items()},
+        "op_ms_median": {k: round(v, 4) for k, v in op_med.items()},
+        "attn_kv_gbps": {o: round(kv_bytes / (op_ms[o] * 1e-3) / 1e9, 1)
+                         for o in ("draft_attn", "verify_attn")},
+        "roofline": {
+            "kernel": f"{dom} (attn_split_kernel + attn_combine_kernel)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": attn_bytes,
+            "mfma_tflops": round(attn_flops / dom_s / 1e12, 1),
+            "mfma_frac": round(attn_flops / dom_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args, case, (qv, kbv, vbv), cons, kv_bytes)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(args, case, vqkv, cons, kv_bytes):
+    """The CPU oracle (fp64 numpy) timed on this host over the same workload:
+    a bounded sample of whole steps (draft + verify attention over every head,
+    both argmaxes, acceptance, commit)."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    qv, kbv, vbv = vqkv
+    f = oracle.from_bf16
+    kp, vp = f(case.k_pages[0]), f(case.v_pages[0])
+    times = []
+    for _ in range(max(1, args.cpu_steps)):
+        t = time.perf_counter()
+        oracle.block_attention(f(case.q), f(case.k_blk), f(case.v_blk), kp, vp, case.block_table,
+                               case.seq_lens, "draft")
+        d = oracle.argmax_rows(cons.logits_d)
+        oracle.block_attention(f(qv), f(kbv), f(vbv), kp, vp, case.block_table, case.seq_lens, "verify")
+        a = oracle.argmax_rows(cons.logits_a)
+        _, n_emit, _ = oracle.accept(d, a)
+        oracle.commit_kv(case.k_pages[:1], case.v_pages[:1], case.block_table, case.seq_lens,
+                         kbv[None], vbv[None], n_emit)
+        times.append(time.perf_counter() - t)
+    sec = statistics.median(times)
+    threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    return {"value": round(2 * kv_bytes / sec / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "seconds_per_step": round(sec, 3),
+            "steps_per_s": round(1.0 / sec, 4),
+            "sample": f"{len(times)} whole steps of the {args.workload} workload (median), "
+                      f"numpy fp64, {threads} BLAS threads on {os.cpu_count()} visible CPUs"}
+
+
+if __name__ == "__main__":
+    main()

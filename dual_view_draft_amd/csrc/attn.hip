@@ -44,6 +44,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef const int32_t __attribute__((address_space(4)))* cptr_i32;
+typedef const void __attribute__((address_space(1)))* gptr_void;
+typedef void __attribute__((address_space(3)))* lptr_void;
+typedef bf16x4 __attribute__((address_space(3)))* lptr_bf16x4;
+
+// 16 zero bytes: the source of tile rows past the last key.
+__device__ __attribute__((aligned(16))) uint16_t g_zero16[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 
 struct AttnArgs {
   const uint16_t* k_pages;
@@ -71,25 +79,13 @@ __device__ __forceinline__ int clamp_len(int L, int max_ctx) {
   return L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
 }
 
-// Token quads inside each 16-token group are stored in the order 0, 2, 1, 3
-// so that the 8 tokens one MFMA lane needs for a P.V k-step are contiguous.
-__device__ __forceinline__ int stored_quad(int qd) {
-  const int lo = qd & 3;
-  return (qd & ~3) | (lo == 1 ? 2 : (lo == 2 ? 1 : lo));
-}
-
-// XOR swizzle of 16-byte granules in the transposed V tile (rows of 64
-// tokens): spreads both the transposing writes and the MFMA reads over the
-// LDS banks.
-__device__ __forceinline__ int vt_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
-
 template <int D, bool VERIFY>
 __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
-  constexpr int KG = D / 8;                     // 16-byte granules per key row
+  constexpr int KG = D / 8;                     // 16-byte granules per key/value row
   constexpr int KS = D / 16;                    // MFMA k-steps of Q.K
   constexpr int DB = D / 32;                    // 32-wide d blocks of O
-  constexpr int KU = (kTile * KG) / 256;        // K-tile granules per thread
-  constexpr int VUNITS = 16 * KG;               // (token quad, granule) units of the V tile
+  constexpr int RPI = 512 / D;                  // rows per 1 KiB wave-wide LDS load
+  constexpr int LPW = KG / 4;                   // LDS loads per wavefront per tile (each of K, V)
   constexpr int TILE_ELEMS = kTile * D;         // bf16 values per K (or V) tile
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2 * TILE_ELEMS];
 
@@ -125,58 +121,50 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
     }
   }
 
-  const int32_t* trow = a.block_table + size_t(b) * a.maxp;
-  // 16 bytes of key/value row `p` (absolute position), granule c.
-  auto fetch16 = [&](const uint16_t* pool, const uint16_t* blk, int p, int c) -> u32x4 {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (p < L) {
-      const int page = trow[p >> 4];
-      if (static_cast<unsigned>(page) < static_cast<unsigned>(a.num_pages))
-        v = *reinterpret_cast<const u32x4*>(
-            pool + ((size_t(page) * a.Hkv + g) * ORTHRUS_PAGE_SIZE + (p & 15)) * D + c * 8);
-    } else if (p < N) {
-      v = *reinterpret_cast<const u32x4*>(blk + ((size_t(b) * a.K + (p - L)) * a.Hkv + g) * D + c * 8);
-    }
-    return v;
-  };
+  // ---- tile loads: HBM -> LDS directly (16 bytes per lane, 1 KiB per
+  // wavefront instruction).  Wavefront w loads tile rows 16w .. 16w+15, i.e.
+  // exactly one cache page, whose id comes through the scalar cache.
+  // K rows keep granule c at c ^ (t % KG); V rows keep it at c ^ 2(t % (KG/2))
+  // (pairs of granules stay together for the transposing reads).
+  const cptr_i32 trow = (cptr_i32)(a.block_table) + size_t(b) * a.maxp;
+  const size_t head_off = size_t(g) * ORTHRUS_PAGE_SIZE * D;
+  const size_t page_stride = size_t(a.Hkv) * ORTHRUS_PAGE_SIZE * D;
+  const size_t blk_row = size_t(a.Hkv) * D;
+  const uint16_t* kblk = a.k_blk + (size_t(b) * a.K * a.Hkv + g) * D;
+  const uint16_t* vblk = a.v_blk + (size_t(b) * a.K * a.Hkv + g) * D;
+  const int lrow = lane / KG;                    // row within one wave load
+  const int lgran = lane % KG;                   // physical granule this lane fills
 
-  u32x4 kreg[KU];
-  u32x4 vreg[4];
-  auto fetch_tile = [&](int ts) {
+  auto issue_tile = [&](int ts, int buf) {
+    const int pidx = min((ts >> 4) + wave, a.maxp - 1);
+    const int page = min(max(trow[pidx], 0), a.num_pages - 1);
+    const uint16_t* kpage = a.k_pages + size_t(page) * page_stride + head_off;
+    const uint16_t* vpage = a.v_pages + size_t(page) * page_stride + head_off;
+    const bool full = ts + kTile <= L;           // uniform: whole tile from the cache
 #pragma unroll
-    for (int j = 0; j < KU; ++j) {
-      const int u = tid + 256 * j;
-      kreg[j] = fetch16(a.k_pages, a.k_blk, ts + u / KG, u % KG);
-    }
-    if (tid < VUNITS) {
-      const int qd = tid & 15, c = tid >> 4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vreg[j] = fetch16(a.v_pages, a.v_blk, ts + qd * 4 + j, c);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = lds[buf];
-    uint16_t* vt = lds[buf] + TILE_ELEMS;
-#pragma unroll
-    for (int j = 0; j < KU; ++j) {
-      const int u = tid + 256 * j;
-      const int t = u / KG, c = u % KG;
-      *reinterpret_cast<u32x4*>(ks + t * D + ((c ^ (t & (KG - 1))) * 8)) = kreg[j];
-    }
-    if (tid < VUNITS) {
-      const int qd = tid & 15, c = tid >> 4;
-      const int sq = stored_quad(qd);
-      const int gs = sq >> 1, hh = sq & 1;
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int w = dd >> 1;
-        const int sh = (dd & 1) * 16;
-        const uint32_t t0 = (vreg[0][w] >> sh) & 0xFFFFu, t1 = (vreg[1][w] >> sh) & 0xFFFFu;
-        const uint32_t t2 = (vreg[2][w] >> sh) & 0xFFFFu, t3 = (vreg[3][w] >> sh) & 0xFFFFu;
-        const int d = c * 8 + dd;
-        u32x2 pair = {t0 | (t1 << 16), t2 | (t3 << 16)};
-        *reinterpret_cast<u32x2*>(vt + d * kTile + ((gs ^ vt_swz(d)) * 8) + hh * 4) = pair;
+    for (int j = 0; j < LPW; ++j) {
+      const int t = 16 * wave + j * RPI + lrow;  // tile row of this lane
+      const int ck = lgran ^ (t & (KG - 1));
+      const int cv = lgran ^ (2 * (t & (KG / 2 - 1)));
+      const uint16_t* ksrc = kpage + (t & 15) * D + ck * 8;
+      const uint16_t* vsrc = vpage + (t & 15) * D + cv * 8;
+      if (!full) {
+        const int p = ts + t;
+        if (p >= L) {
+          if (p < N) {
+            ksrc = kblk + (p - L) * blk_row + ck * 8;
+            vsrc = vblk + (p - L) * blk_row + cv * 8;
+          } else {
+            ksrc = g_zero16;
+            vsrc = g_zero16;
+          }
+        }
       }
+      const int n = wave * LPW + j;              // 1 KiB slot of this load
+      __builtin_amdgcn_global_load_lds((const gptr_void)ksrc,
+                                       (lptr_void)(&lds[buf][n * 512]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const gptr_void)vsrc,
+                                       (lptr_void)(&lds[buf][TILE_ELEMS + n * 512]), 16, 0, 0);
     }
   };
 
@@ -188,29 +176,37 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
   float l_run = 0.f;
   const int row_limit = VERIFY ? (L + i_row) : (N - 1);  // last visible position
 
-  fetch_tile(start);
-  store_tile(0);
+  // lane constants of the transposing V reads: lane (group G = lane/16, k = lane%16)
+  const int trk = lane & 15;
+  const int tr_dofs = 16 * ((lane >> 4) & 1) + 4 * (trk & 3);   // + db*32
+  const int tr_tofs = 4 * half + (trk >> 2);                      // + tb*32 + 16*k2 (+8)
+
+  issue_tile(start, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0): this wave's loads landed
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int cur = t & 1;
     const int ts = start + t * kTile;
-    if (t + 1 < ntiles) fetch_tile(ts + kTile);
+    if (t + 1 < ntiles) issue_tile(ts + kTile, cur ^ 1);
 
     if (wave_rows) {
       const uint16_t* ks = lds[cur];
-      const uint16_t* vt = lds[cur] + TILE_ELEMS;
+      const uint16_t* vs = lds[cur] + TILE_ELEMS;
       f32x16 sacc[2];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         sacc[tb] = f32x16{};
         const int tok = tb * 32 + col;
+        bf16x8 kf[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
           const int gk = kk * 2 + half;
-          const bf16x8 kv = *reinterpret_cast<const bf16x8*>(ks + tok * D + ((gk ^ (tok & (KG - 1))) * 8));
-          sacc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[kk], sacc[tb], 0, 0, 0);
+          kf[kk] = *reinterpret_cast<const bf16x8*>(ks + tok * D + ((gk ^ (tok & (KG - 1))) * 8));
         }
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          sacc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qreg[kk], sacc[tb], 0, 0, 0);
       }
       // scores in log2 units; mask what this row may not see
       const bool need_mask = ts + kTile - 1 > row_limit;   // per lane
@@ -244,8 +240,10 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
       }
       l_run = l_run * alpha + lsum;
       m_run = m_new;
+      if (__any(alpha != 1.0f)) {        // skipped once no row's maximum moves
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      }
 
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
@@ -254,18 +252,25 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
           bf16x8 pb;
 #pragma unroll
           for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(sacc[tb][8 * k2 + j]);
-          const int gs = tb * 4 + k2 * 2 + half;
+          const int t1 = tb * 32 + 16 * k2 + tr_tofs;       // rows t1 and t1 + 8
+          const int sw = 2 * (t1 & (KG / 2 - 1));            // same for t1 + 8
+          bf16x8 vf[DB];
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const int d = db * 32 + col;
-            const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vt + d * kTile + ((gs ^ vt_swz(d)) * 8));
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb, oacc[db], 0, 0, 0);
+            const int d = db * 32 + tr_dofs;
+            const int off = ((((d >> 3) ^ sw) * 8) + (d & 4));
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lptr_bf16x4)(vs + t1 * D + off));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lptr_bf16x4)(vs + (t1 + 8) * D + off));
+            vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           }
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb, oacc[db], 0, 0, 0);
         }
       }
     }
 
-    if (t + 1 < ntiles) store_tile(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): next tile's loads landed
     __syncthreads();
   }
 
@@ -294,15 +299,22 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Merge the split partials of every output row in increasing split order:
+// Merge the split partials of every output row:
 //   out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
+// One wavefront per output row: D/4 lanes cover the row (4 values each) and
+// the 64/(D/4) lane groups take interleaved splits s = group, group + SG, ...
+// in increasing order; the group sums are then added in group order.  Splits
+// a row cannot see contribute exact zeros, so the result does not depend on
+// how many splits the call had.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
-  constexpr int TPR = D / 4;  // threads per output row, 4 values each
-  const int gid = blockIdx.x * 256 + threadIdx.x;
-  const int orow = gid / TPR;                       // (b, i, h) flattened
-  if (orow >= a.B * a.K * a.Hq) return;
-  const int d0 = (gid % TPR) * 4;
+  constexpr int TPR = D / 4;      // lanes per row slice
+  constexpr int SG = 64 / TPR;    // split groups per wavefront
+  const int lane = threadIdx.x & 63;
+  const int orow = blockIdx.x * 4 + (threadIdx.x >> 6);   // (b, i, h) flattened
+  if (orow >= a.B * a.K * a.Hq) return;                    // uniform per wavefront
+  const int sg = lane / TPR;
+  const int d0 = (lane % TPR) * 4;
   const int h = orow % a.Hq;
   const int bi = orow / a.Hq;
   const int i = bi % a.K;
@@ -314,22 +326,41 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
   const int L = clamp_len(a.seq_lens[b], a.max_ctx);
   const int ns = (L + a.K + a.split - 1) / a.split;
   const int Hkv = a.Hq / a.G;
-  const size_t part0 = ((size_t(b) * Hkv + g) * a.nchunks + chunk) * a.nsplit;
+  const size_t prow0 = ((size_t(b) * Hkv + g) * a.nchunks + chunk) * a.nsplit * a.rpc + rl;
+  const float* ml = a.part_ml + prow0 * 2;
+  const float* po = a.part_o + prow0 * D + d0;
+  const size_t ml_stride = size_t(a.rpc) * 2, o_stride = size_t(a.rpc) * D;
 
   float M = -__builtin_inff();
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[((part0 + s) * a.rpc + rl) * 2]);
+#pragma unroll 4
+  for (int s = sg; s < ns; s += SG) M = fmaxf(M, ml[s * ml_stride]);
+#pragma unroll
+  for (int off = TPR; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const size_t prow = (part0 + s) * a.rpc + rl;
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[prow * 2] - M);
-    const f32x4 o = *reinterpret_cast<const f32x4*>(a.part_o + prow * D + d0);
+#pragma unroll 4
+  for (int s = sg; s < ns; s += SG) {
+    const float w = __builtin_amdgcn_exp2f(ml[s * ml_stride] - M);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(po + s * o_stride);
     acc += w * o;
-    lsum += w * a.part_ml[prow * 2 + 1];
+    lsum += w * ml[s * ml_stride + 1];
   }
-  const float inv = 1.0f / lsum;
-  u32x2 packed = {bf16_rne_bits(acc[0] * inv) | (bf16_rne_bits(acc[1] * inv) << 16),
-                  bf16_rne_bits(acc[2] * inv) | (bf16_rne_bits(acc[3] * inv) << 16)};
+  f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+  float ltot = 0.f;
+#pragma unroll
+  for (int k = 0; k < SG; ++k) {
+    const int src = (lane % TPR) + k * TPR;
+    tot[0] += __shfl(acc[0], src);
+    tot[1] += __shfl(acc[1], src);
+    tot[2] += __shfl(acc[2], src);
+    tot[3] += __shfl(acc[3], src);
+    ltot += __shfl(lsum, src);
+  }
+  if (sg != 0) return;
+  const float inv = 1.0f / ltot;
+  u32x2 packed = {bf16_rne_bits(tot[0] * inv) | (bf16_rne_bits(tot[1] * inv) << 16),
+                  bf16_rne_bits(tot[2] * inv) | (bf16_rne_bits(tot[3] * inv) << 16)};
   *reinterpret_cast<u32x2*>(a.out + size_t(orow) * D + d0) = packed;
 }
 
@@ -370,8 +401,8 @@ hipError_t launch_attention(const AttnPlan& p, const orthrus_kv& kv, const void*
   c.out = static_cast<uint16_t*>(out);
   c.B = p.B; c.K = p.K; c.Hq = p.Hq; c.G = p.G; c.max_ctx = p.max_ctx;
   c.split = p.split; c.nsplit = p.nsplit; c.nchunks = p.nchunks; c.rpc = p.rows_per_chunk;
-  const int64_t threads = int64_t(p.B) * p.K * p.Hq * (p.D / 4);
-  dim3 grid(unsigned((threads + 255) / 256));
+  const int64_t rows = int64_t(p.B) * p.K * p.Hq;
+  dim3 grid(unsigned((rows + 3) / 4));
   return p.D == 128 ? launch_kernel(&attn_combine_kernel<128>, grid, dim3(256), stream, c)
                     : launch_kernel(&attn_combine_kernel<64>, grid, dim3(256), stream, c);
 }

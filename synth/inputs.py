@@ -24,7 +24,7 @@ import numpy as np
 
 __all__ = [
     "BF16_NAN", "BF16_SENTINEL", "f32_to_bf16_bits", "bf16_bits_to_f32",
-    "PagedCase", "make_paged_case", "ConsensusCase", "make_consensus_case",
+    "PagedCase", "make_paged_case", "make_block_qkv", "ConsensusCase", "make_consensus_case",
     "draw_accept_lengths", "make_tie_logits", "ToyConfig", "TOY_CFG5",
     "TOY_TINY", "make_toy_weights", "make_prompt", "WORKLOADS",
 ]
@@ -141,6 +141,16 @@ def make_paged_case(seed: int, B: int, K: int, Hq: int, Hkv: int, D: int,
                 v_pages[layer, page, :, :n, :] = vc[p0:p0 + n].transpose(1, 0, 2)
     return PagedCase(B, K, Hq, Hkv, D, page_size, layers, q, k_blk, v_blk,
                      k_pages, v_pages, table, seq_lens, num_pages, fill_bits, needles)
+
+
+def make_block_qkv(seed: int, B: int, K: int, Hq: int, Hkv: int, D: int, std: float | None = None):
+    """Another set of block rows (q [B,K,Hq,D], k_blk, v_blk [B,K,Hkv,D], bf16
+    bits): the verify pass uses the AR view's projections, which differ from
+    the draft pass's diffusion-view projections."""
+    rng = np.random.default_rng(seed)
+    std = 1.0 / math.sqrt(D) if std is None else std
+    return (_normal_bf16(rng, (B, K, Hq, D), std), _normal_bf16(rng, (B, K, Hkv, D), std),
+            _normal_bf16(rng, (B, K, Hkv, D), std))
 
 
 def _plant_needles(rng, q_bits, k_blk_bits, kc, b, L, K, G, Hkv, D, P, needles):
