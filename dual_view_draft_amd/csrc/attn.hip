@@ -79,22 +79,79 @@ __device__ __forceinline__ int clamp_len(int L, int max_ctx) {
   return L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
 }
 
+// Workgroup barrier without a memory fence: no wait for outstanding global
+// loads is implied (the tile ring waits for exactly the loads it needs); the
+// empty asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits [3:0] and [15:14], expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Wait until at most `n * PER` vector-memory instructions of this wavefront
+// are outstanding (n is uniform and < 8).
+template <int PER>
+__device__ __forceinline__ void wait_tiles_outstanding(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<PER>(); break;
+    case 2: wait_vmcnt<2 * PER>(); break;
+    case 3: wait_vmcnt<3 * PER>(); break;
+    case 4: wait_vmcnt<4 * PER>(); break;
+    case 5: wait_vmcnt<5 * PER>(); break;
+    default: wait_vmcnt<6 * PER>(); break;
+  }
+}
+
+template <int D>
+struct SplitCfg {
+  static constexpr int KG = D / 8;                 // 16-byte granules per key/value row
+  static constexpr int NS = 4;                     // LDS ring stages
+  static constexpr int TILE_ELEMS = kTile * D;     // bf16 values per K (or V) tile
+  static constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;
+  static constexpr int RPI = 512 / D;              // tile rows per 1 KiB wave-wide LDS load
+  static constexpr int LPR = 8 / RPI;              // such loads per 8 rows of one tensor
+  static constexpr int LPT = 2 * LPR;              // loads per wavefront per tile (K and V)
+};
+
+// One workgroup = 8 wavefronts on one CU: wavefront w owns query rows
+// 32*(w%4) .. +31 of its row chunk and tokens 32*(w/4) .. +31 of every
+// 64-token tile; the two token halves keep separate softmax states that are
+// merged in LDS at the end.  Tiles stream through an NS-stage LDS ring so
+// that NS-1 tiles are in flight while one is being computed.
 template <int D, bool VERIFY>
-__global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
-  constexpr int KG = D / 8;                     // 16-byte granules per key/value row
+__global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
+  using C = SplitCfg<D>;
+  constexpr int KG = C::KG, NS = C::NS, TILE_ELEMS = C::TILE_ELEMS;
+  constexpr int STAGE_ELEMS = C::STAGE_ELEMS, RPI = C::RPI, LPR = C::LPR, LPT = C::LPT;
   constexpr int KS = D / 16;                    // MFMA k-steps of Q.K
   constexpr int DB = D / 32;                    // 32-wide d blocks of O
-  constexpr int RPI = 512 / D;                  // rows per 1 KiB wave-wide LDS load
-  constexpr int LPW = KG / 4;                   // LDS loads per wavefront per tile (each of K, V)
-  constexpr int TILE_ELEMS = kTile * D;         // bf16 values per K (or V) tile
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2 * TILE_ELEMS];
+  // One array per ring stage, always indexed with compile-time stage numbers:
+  // the compiler can then tell that reading one stage does not depend on the
+  // DMA still writing another, and inserts no wait for it.
+  static_assert(NS == 4, "ring of four stages");
+  __shared__ __attribute__((aligned(16))) uint16_t st0[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t st1[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t st2[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t st3[STAGE_ELEMS];
+  uint16_t* const stage_buf[NS] = {st0, st1, st2, st3};
 
   const int s = blockIdx.x;
   const int g = blockIdx.y / a.nchunks;
   const int chunk = blockIdx.y - g * a.nchunks;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
+  const int rg = wave & 3, th = wave >> 2;      // row group, token half
 
   const int L = clamp_len(a.seq_lens[b], a.max_ctx);
   const int N = L + a.K;                         // keys that exist for this sequence
@@ -104,8 +161,8 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
   const int ntiles = (end - start + kTile - 1) / kTile;
 
   // ---- this lane's query row ---------------------------------------------
-  const bool wave_rows = wave * kRowsPerWave < a.rpc;          // wave-uniform
-  const int r = chunk * kMaxRowsPerCta + wave * kRowsPerWave + col;
+  const bool wave_rows = rg * kRowsPerWave < a.rpc;            // wave-uniform
+  const int r = chunk * kMaxRowsPerCta + rg * kRowsPerWave + col;
   const bool row_ok = wave_rows && r < a.rows;
   const int i_row = row_ok ? r / a.G : 0;
   const int gg = row_ok ? r - i_row * a.G : 0;
@@ -121,175 +178,207 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
     }
   }
 
-  // ---- tile loads: HBM -> LDS directly (16 bytes per lane, 1 KiB per
-  // wavefront instruction).  Wavefront w loads tile rows 16w .. 16w+15, i.e.
-  // exactly one cache page, whose id comes through the scalar cache.
+  // ---- tile loads: HBM -> LDS directly, 16 bytes per lane, 1 KiB per
+  // wavefront instruction.  Wavefront w loads tile rows 8w .. 8w+7 of K and
+  // of V: half of one cache page, whose id comes through the scalar cache.
   // K rows keep granule c at c ^ (t % KG); V rows keep it at c ^ 2(t % (KG/2))
-  // (pairs of granules stay together for the transposing reads).
+  // (granule pairs stay together for the transposing reads).
   const cptr_i32 trow = (cptr_i32)(a.block_table) + size_t(b) * a.maxp;
-  const size_t head_off = size_t(g) * ORTHRUS_PAGE_SIZE * D;
   const size_t page_stride = size_t(a.Hkv) * ORTHRUS_PAGE_SIZE * D;
   const size_t blk_row = size_t(a.Hkv) * D;
+  const int lrow = lane / KG;                    // row within one 1 KiB load
+  const int lgran = lane % KG;                   // physical granule this lane fills
+  // byte offsets of this lane inside its half page (constant over tiles)
+  uint32_t koff[LPR], voff[LPR];
+  int trow_of[LPR];
+#pragma unroll
+  for (int j = 0; j < LPR; ++j) {
+    const int t = 8 * wave + j * RPI + lrow;     // tile row
+    trow_of[j] = t;
+    const int ck = lgran ^ (t & (KG - 1));
+    const int cv = lgran ^ (2 * (t & (KG / 2 - 1)));
+    koff[j] = uint32_t(((t & 15) * D + ck * 8) * 2);
+    voff[j] = uint32_t(((t & 15) * D + cv * 8) * 2);
+  }
+  const char* kpool = reinterpret_cast<const char*>(a.k_pages + size_t(g) * ORTHRUS_PAGE_SIZE * D);
+  const char* vpool = reinterpret_cast<const char*>(a.v_pages + size_t(g) * ORTHRUS_PAGE_SIZE * D);
   const uint16_t* kblk = a.k_blk + (size_t(b) * a.K * a.Hkv + g) * D;
   const uint16_t* vblk = a.v_blk + (size_t(b) * a.K * a.Hkv + g) * D;
-  const int lrow = lane / KG;                    // row within one wave load
-  const int lgran = lane % KG;                   // physical granule this lane fills
 
-  auto issue_tile = [&](int ts, int buf) {
-    const int pidx = min((ts >> 4) + wave, a.maxp - 1);
+  auto issue_tile = [&](int ts, uint16_t* sbuf) {
+    const int pidx = min((ts >> 4) + (wave >> 1), a.maxp - 1);
     const int page = min(max(trow[pidx], 0), a.num_pages - 1);
-    const uint16_t* kpage = a.k_pages + size_t(page) * page_stride + head_off;
-    const uint16_t* vpage = a.v_pages + size_t(page) * page_stride + head_off;
-    const bool full = ts + kTile <= L;           // uniform: whole tile from the cache
+    const char* kbase = kpool + size_t(page) * page_stride * 2;
+    const char* vbase = vpool + size_t(page) * page_stride * 2;
+    uint16_t* dst = sbuf + wave * LPR * 512;
+    if (ts + kTile <= L) {                       // uniform: whole tile from the cache
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int t = 16 * wave + j * RPI + lrow;  // tile row of this lane
-      const int ck = lgran ^ (t & (KG - 1));
-      const int cv = lgran ^ (2 * (t & (KG / 2 - 1)));
-      const uint16_t* ksrc = kpage + (t & 15) * D + ck * 8;
-      const uint16_t* vsrc = vpage + (t & 15) * D + cv * 8;
-      if (!full) {
-        const int p = ts + t;
-        if (p >= L) {
-          if (p < N) {
-            ksrc = kblk + (p - L) * blk_row + ck * 8;
-            vsrc = vblk + (p - L) * blk_row + cv * 8;
-          } else {
-            ksrc = g_zero16;
-            vsrc = g_zero16;
-          }
-        }
+      for (int j = 0; j < LPR; ++j) {
+        __builtin_amdgcn_global_load_lds((gptr_void)(kbase + koff[j]), (lptr_void)(dst + j * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gptr_void)(vbase + voff[j]),
+                                         (lptr_void)(dst + TILE_ELEMS + j * 512), 16, 0, 0);
       }
-      const int n = wave * LPW + j;              // 1 KiB slot of this load
-      __builtin_amdgcn_global_load_lds((const gptr_void)ksrc,
-                                       (lptr_void)(&lds[buf][n * 512]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const gptr_void)vsrc,
-                                       (lptr_void)(&lds[buf][TILE_ELEMS + n * 512]), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < LPR; ++j) {
+        const int p = ts + trow_of[j];
+        const void* ks = kbase + koff[j];
+        const void* vs = vbase + voff[j];
+        if (p >= L) {
+          const int ck = lgran ^ (trow_of[j] & (KG - 1));
+          const int cv = lgran ^ (2 * (trow_of[j] & (KG / 2 - 1)));
+          ks = p < N ? static_cast<const void*>(kblk + (p - L) * blk_row + ck * 8) : g_zero16;
+          vs = p < N ? static_cast<const void*>(vblk + (p - L) * blk_row + cv * 8) : g_zero16;
+        }
+        __builtin_amdgcn_global_load_lds((gptr_void)ks, (lptr_void)(dst + j * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gptr_void)vs, (lptr_void)(dst + TILE_ELEMS + j * 512), 16, 0, 0);
+      }
     }
   };
 
-  // ---- running softmax state (per lane = per query row) ------------------
+  // ---- running softmax state (per lane = per query row, this token half) --
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  // m_run is a lazily raised reference maximum (log2 units): it only moves
+  // when a score exceeds it by more than 2^8, so P <= 256 and O is rarely
+  // rescaled.  The result depends only on this row's own scores.
   float m_run = -__builtin_inff();
   float l_run = 0.f;
   const int row_limit = VERIFY ? (L + i_row) : (N - 1);  // last visible position
+  const float c = a.scale_log2;
 
-  // lane constants of the transposing V reads: lane (group G = lane/16, k = lane%16)
   const int trk = lane & 15;
   const int tr_dofs = 16 * ((lane >> 4) & 1) + 4 * (trk & 3);   // + db*32
-  const int tr_tofs = 4 * half + (trk >> 2);                      // + tb*32 + 16*k2 (+8)
+  const int tr_tofs = 4 * half + (trk >> 2);                      // + th*32 + 16*k2 (+8)
 
-  issue_tile(start, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0): this wave's loads landed
-  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k)
+    if (k < ntiles) issue_tile(start + k * kTile, stage_buf[k]);
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    const int ts = start + t * kTile;
-    if (t + 1 < ntiles) issue_tile(ts + kTile, cur ^ 1);
-
-    if (wave_rows) {
-      const uint16_t* ks = lds[cur];
-      const uint16_t* vs = lds[cur] + TILE_ELEMS;
-      f32x16 sacc[2];
+  for (int t0 = 0; t0 < ntiles; t0 += NS) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        sacc[tb] = f32x16{};
-        const int tok = tb * 32 + col;
-        bf16x8 kf[KS];
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const int gk = kk * 2 + half;
-          kf[kk] = *reinterpret_cast<const bf16x8*>(ks + tok * D + ((gk ^ (tok & (KG - 1))) * 8));
-        }
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-          sacc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qreg[kk], sacc[tb], 0, 0, 0);
-      }
-      // scores in log2 units; mask what this row may not see
-      const bool need_mask = ts + kTile - 1 > row_limit;   // per lane
-      float tmax = -__builtin_inff();
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float sc = sacc[tb][v] * a.scale_log2;
-          if (need_mask) {
-            const int pos = ts + tb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-            if (pos > row_limit) sc = -__builtin_inff();
+    for (int k = 0; k < NS; ++k) {
+      const int t = t0 + k;
+      if (t >= ntiles) break;                                      // uniform
+      const int ts = start + t * kTile;
+      uint16_t* const sbuf = stage_buf[k];
+      wait_tiles_outstanding<LPT>(min(NS - 2, ntiles - 1 - t));   // tile t has landed
+      lds_barrier();                                               // ... for every wavefront
+      if (t + NS - 1 < ntiles) issue_tile(ts + (NS - 1) * kTile, stage_buf[(k + NS - 1) % NS]);
+        if (wave_rows) {
+          const uint16_t* ks = sbuf;
+          const uint16_t* vs = ks + TILE_ELEMS;
+          f32x16 sacc = f32x16{};
+          {
+            const int tok = th * 32 + col;
+            bf16x8 kf[KS];
+    #pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+              const int gk = kk * 2 + half;
+              kf[kk] = *reinterpret_cast<const bf16x8*>(ks + tok * D + ((gk ^ (tok & (KG - 1))) * 8));
+            }
+    #pragma unroll
+            for (int kk = 0; kk < KS; ++kk)
+              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qreg[kk], sacc, 0, 0, 0);
           }
-          sacc[tb][v] = sc;
-          tmax = fmaxf(tmax, sc);
-        }
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float lsum = 0.f;
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float pv = __builtin_amdgcn_exp2f(sacc[tb][v] - m_use);
-          sacc[tb][v] = pv;
-          lsum += pv;
-        }
-      }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-      if (__any(alpha != 1.0f)) {        // skipped once no row's maximum moves
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      }
-
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          bf16x8 pb;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(sacc[tb][8 * k2 + j]);
-          const int t1 = tb * 32 + 16 * k2 + tr_tofs;       // rows t1 and t1 + 8
-          const int sw = 2 * (t1 & (KG / 2 - 1));            // same for t1 + 8
-          bf16x8 vf[DB];
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int d = db * 32 + tr_dofs;
-            const int off = ((((d >> 3) ^ sw) * 8) + (d & 4));
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lptr_bf16x4)(vs + t1 * D + off));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lptr_bf16x4)(vs + (t1 + 8) * D + off));
-            vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          // mask what this row may not see (raw scores; the scale is positive)
+          const int tok0 = ts + th * 32;
+          if (tok0 + 31 > row_limit) {
+    #pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int pos = tok0 + 8 * (v >> 2) + 4 * half + (v & 3);
+              if (pos > row_limit) sacc[v] = -__builtin_inff();
+            }
           }
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb, oacc[db], 0, 0, 0);
+          float tmax = -__builtin_inff();
+    #pragma unroll
+          for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[v]);
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c;
+          const float m_new = tmax > m_run + 8.0f ? tmax : m_run;
+          const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+          float lsum = 0.f;
+    #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c, -m_use));
+            sacc[v] = pv;
+            lsum += pv;
+          }
+          if (__any(m_new != m_run)) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            l_run *= alpha;
+    #pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+          }
+          l_run += lsum;
+          m_run = m_new;
+
+    #pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            bf16x8 pb;
+    #pragma unroll
+            for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(sacc[8 * k2 + j]);
+            const int t1 = th * 32 + 16 * k2 + tr_tofs;        // rows t1 and t1 + 8
+            const int sw = 2 * (t1 & (KG / 2 - 1));             // same for t1 + 8
+            bf16x8 vf[DB];
+    #pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const int d = db * 32 + tr_dofs;
+              const int off = ((((d >> 3) ^ sw) * 8) + (d & 4));
+              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lptr_bf16x4)(vs + t1 * D + off));
+              const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lptr_bf16x4)(vs + (t1 + 8) * D + off));
+              vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+    #pragma unroll
+            for (int db = 0; db < DB; ++db)
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb, oacc[db], 0, 0, 0);
+          }
         }
-      }
     }
-
-    __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): next tile's loads landed
-    __syncthreads();
   }
 
-  if (!wave_rows) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // ---- merge the two token halves of each row group through LDS ----------
+  l_run += __shfl_xor(l_run, 32);
+  lds_barrier();                                   // every wavefront is done with the ring
+  float* xo = reinterpret_cast<float*>(rg == 0 ? st0 : rg == 1 ? st1 : rg == 2 ? st2 : st3);
+  float* xml = xo + kRowsPerWave * D;
+  if (wave_rows && th == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 o4 = {oacc[db][4 * j + 0], oacc[db][4 * j + 1], oacc[db][4 * j + 2], oacc[db][4 * j + 3]};
+        *reinterpret_cast<f32x4*>(xo + col * D + db * 32 + 8 * j + 4 * half) = o4;
+      }
+    if (half == 0) {
+      xml[col] = m_run;
+      xml[kRowsPerWave + col] = l_run;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): exchange writes done
+  lds_barrier();
+  if (!wave_rows || th == 1) return;
+  const float m_b = xml[col], l_b = xml[kRowsPerWave + col];
+  const float M = fmaxf(m_run, m_b);
+  const float M_use = (M == -__builtin_inff()) ? 0.f : M;
+  const float wa = __builtin_amdgcn_exp2f(m_run - M_use);
+  const float wb = __builtin_amdgcn_exp2f(m_b - M_use);
   const size_t part = ((size_t(b) * a.Hkv + g) * a.nchunks + chunk) * a.nsplit + s;
-  const size_t prow = part * a.rpc + wave * kRowsPerWave + col;
+  const size_t prow = part * a.rpc + rg * kRowsPerWave + col;
   float* po = a.part_o + prow * D;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f32x4 o4 = {oacc[db][4 * j + 0], oacc[db][4 * j + 1], oacc[db][4 * j + 2], oacc[db][4 * j + 3]};
+      const f32x4 ob = *reinterpret_cast<const f32x4*>(xo + col * D + db * 32 + 8 * j + 4 * half);
+      f32x4 o4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] = wa * oacc[db][4 * j + i] + wb * ob[i];
       *reinterpret_cast<f32x4*>(po + db * 32 + 8 * j + 4 * half) = o4;
     }
-  }
   if (half == 0) {
-    a.part_ml[prow * 2 + 0] = m_run;
-    a.part_ml[prow * 2 + 1] = l_tot;
+    a.part_ml[prow * 2 + 0] = M;
+    a.part_ml[prow * 2 + 1] = wa * l_run + wb * l_b;
   }
 }
 
@@ -367,7 +456,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
 template <int D, bool VERIFY>
 hipError_t launch_split(const AttnArgs& a, hipStream_t stream) {
   dim3 grid(a.nsplit, a.Hkv * a.nchunks, a.B);
-  return launch_kernel(&attn_split_kernel<D, VERIFY>, grid, dim3(256), stream, a);
+  return launch_kernel(&attn_split_kernel<D, VERIFY>, grid, dim3(512), stream, a);
 }
 
 }  // namespace

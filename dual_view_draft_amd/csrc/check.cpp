@@ -47,12 +47,14 @@ const char* status_string(int status) {
 
 int attn_split_tokens(int B, int Hkv, int max_ctx) {
   if (B < 1 || Hkv < 1 || max_ctx < 0) return kTile * 4;
-  // Aim for about two workgroups per compute unit (256 CUs) when every
-  // sequence is max_ctx long; splits stay between 4 and 64 tiles long.
+  // One 8-wavefront workgroup fills a CU (256 CUs).  A single sequence is cut
+  // into about one split per CU; a batch (whose lengths the host does not
+  // know) into about four per CU, so that short and long sequences balance.
   const int64_t work = int64_t(B) * Hkv * (int64_t(max_ctx) + kTile);
-  int64_t s = round_up(ceil_div(work, 512), kTile);
-  if (s < 4 * kTile) s = 4 * kTile;
-  if (s > 64 * kTile) s = 64 * kTile;
+  const int64_t target = B == 1 ? 256 : 1024;
+  int64_t s = round_up(ceil_div(work, target), kTile);
+  if (s < 2 * kTile) s = 2 * kTile;
+  if (s > 1024 * kTile) s = 1024 * kTile;
   return int(s);
 }
 

@@ -7,7 +7,7 @@
 #include <cstdint>
 #include <string>
 
-#include "../../include/orthrus.h"
+#include "orthrus.h"
 
 namespace orthrus {
 
