@@ -5,30 +5,38 @@
 // Token Generation via Dual-View Diffusion", section 2.1).  The draft pass
 // (diffusion view) lets every block row see the whole cache and every other
 // block row (section 2.2, block mask); the verify pass (AR view) is causal
-// inside the block (section 2.3 step 2).  Both are the same kernel with a
+// inside the block (section 2.3 step 2).  Both are this kernel with a
 // compile-time mask.
 //
 // Work decomposition (flash-decoding style split context):
-//   grid = (context split s, KV head g x row chunk, sequence b)
-//   Each workgroup owns the G*K query rows of KV head g (up to 128 rows per
-//   chunk, 32 rows per wavefront) and streams the keys/values at absolute
-//   positions [s*split, (s+1)*split) through LDS in 64-token tiles (4 pages),
-//   so every K/V byte is read from HBM once and shared by all rows of the
-//   group.  Positions < L_b come from the pages via the block table, positions
-//   L_b .. L_b+K-1 from the block's own k_blk/v_blk, later positions are zero.
-//   Split boundaries and tiles are fixed in absolute position, so a row's
-//   arithmetic is independent of K and of the other rows present.
+//   grid = (context split s, KV head g x row chunk, sequence b), one
+//   8-wavefront workgroup per CU.  A workgroup owns the G*K query rows of KV
+//   head g (up to 128 rows per chunk) and streams the keys/values at absolute
+//   positions [s*split, (s+1)*split) in 64-token tiles (4 pages), so every K/V
+//   byte is read from HBM once and shared by all rows of the group.  Positions
+//   < L_b come from the pages via the block table, positions L_b .. L_b+K-1
+//   from the block's own k_blk/v_blk, later positions are zero.  Splits and
+//   tiles sit at fixed absolute positions, so a row's arithmetic does not
+//   depend on K or on the other rows present.
 //
-// Per tile and wavefront (S^T formulation, 32x32x16 bf16 MFMA, fp32 accum):
-//   S^T[token][row] = K_tile . Q^T     A = K tile from LDS, B = Q in registers
-//     -> lane l holds one query row (l % 32) and 32 of the tile's 64 scores,
-//        so the softmax max/sum are in-lane plus one exchange with lane l^32.
-//   O^T[d][row]    += V^T . P^T        A = V^T tile from LDS, B = P (bf16)
-//     -> P^T comes straight out of the S^T accumulator registers; the V tile is
-//        transposed while being written to LDS, in the token order that matches.
-//   Online softmax in fp32 with exp2 (log2(e) folded into the scale).
-// The partial (m, l, O) of every split goes to the workspace; a second kernel
-// merges the splits in fixed order and writes bf16.
+// Memory path: tiles go HBM -> LDS directly (16-byte global_load_lds per lane,
+// 1 KiB per wavefront instruction) through a 4-stage LDS ring, so three tiles
+// (96 KiB for head_dim 128) are in flight while one is computed.  Each
+// wavefront fetches half of one page of K and of V per tile; page ids come
+// from the block table once per split.
+//
+// Compute per tile (wavefront w: rows 32*(w%4)+0..31, tokens 32*(w/4)+0..31):
+//   S^T[token][row] = K . Q^T   32x32x16 bf16 MFMA, A = K from LDS, B = Q in
+//                               registers; a lane holds one query row, so the
+//                               softmax max/sum are in-lane plus one exchange
+//                               with lane l^32 (v_permlane32_swap).
+//   O^T[d][row]    += V^T . P^T  A = V^T read transposed from LDS with
+//                               ds_read_b64_tr_b16, B = P (bf16) taken straight
+//                               from the S^T accumulators.
+//   Online softmax in fp32 with exp2 (log2 e folded into the scale).  The two
+//   token halves keep separate states, merged in LDS at the end of the split.
+// Each split stores O/l as bf16 plus (m, l) in fp32; a second kernel merges
+// the splits in a fixed order and writes bf16.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -40,11 +48,11 @@ namespace orthrus {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef const int32_t __attribute__((address_space(4)))* cptr_i32;
 typedef const void __attribute__((address_space(1)))* gptr_void;
 typedef void __attribute__((address_space(3)))* lptr_void;
@@ -61,14 +69,14 @@ struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k_blk;
   const uint16_t* v_blk;
-  float* part_o;   // [B][Hkv][nchunks][nsplit][rpc][D]
-  float* part_ml;  // [B][Hkv][nchunks][nsplit][rpc][2]  (running max m in log2 units, sum l)
+  uint16_t* part_o;  // [B][Hkv][nchunks][nsplit][rpc][D] bf16: O / l of the split
+  float* part_ml;    // [B][Hkv][nchunks][nsplit][rpc][2]: m (log2 units), l
   int B, K, Hq, Hkv, G, num_pages, maxp, max_ctx, split, nsplit, rows, nchunks, rpc;
   float scale_log2;
 };
 
 struct CombineArgs {
-  const float* part_o;
+  const uint16_t* part_o;
   const float* part_ml;
   const int32_t* seq_lens;
   uint16_t* out;  // [B][K][Hq][D] bf16
@@ -77,6 +85,28 @@ struct CombineArgs {
 
 __device__ __forceinline__ int clamp_len(int L, int max_ctx) {
   return L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
+}
+
+// Two floats -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Combine a value with the one in lane l ^ 32 (v_permlane32_swap): both
+// halves receive the pair, so max and sum come out bitwise identical in
+// lanes l and l ^ 32 (the low half's value is always the first operand).
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Workgroup barrier without a memory fence: no wait for outstanding global
@@ -96,19 +126,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-// Wait until at most `n * PER` vector-memory instructions of this wavefront
-// are outstanding (n is uniform and < 8).
+// Wait until at most n * PER vector-memory instructions of this wavefront are
+// outstanding (n uniform, 0..2).  Vector loads complete in issue order.
 template <int PER>
 __device__ __forceinline__ void wait_tiles_outstanding(int n) {
-  switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<PER>(); break;
-    case 2: wait_vmcnt<2 * PER>(); break;
-    case 3: wait_vmcnt<3 * PER>(); break;
-    case 4: wait_vmcnt<4 * PER>(); break;
-    case 5: wait_vmcnt<5 * PER>(); break;
-    default: wait_vmcnt<6 * PER>(); break;
-  }
+  if (n >= 2) wait_vmcnt<2 * PER>();
+  else if (n == 1) wait_vmcnt<PER>();
+  else wait_vmcnt<0>();
 }
 
 template <int D>
@@ -122,11 +146,6 @@ struct SplitCfg {
   static constexpr int LPT = 2 * LPR;              // loads per wavefront per tile (K and V)
 };
 
-// One workgroup = 8 wavefronts on one CU: wavefront w owns query rows
-// 32*(w%4) .. +31 of its row chunk and tokens 32*(w/4) .. +31 of every
-// 64-token tile; the two token halves keep separate softmax states that are
-// merged in LDS at the end.  Tiles stream through an NS-stage LDS ring so
-// that NS-1 tiles are in flight while one is being computed.
 template <int D, bool VERIFY>
 __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   using C = SplitCfg<D>;
@@ -158,38 +177,18 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   const int start = s * a.split;
   if (start >= N) return;                        // uniform across the workgroup
   const int end = min(start + a.split, N);
-  const int ntiles = (end - start + kTile - 1) / kTile;
+  const int ntiles = (end - start + kTile - 1) / kTile;   // <= kMaxSplitTiles
 
-  // ---- this lane's query row ---------------------------------------------
-  const bool wave_rows = rg * kRowsPerWave < a.rpc;            // wave-uniform
-  const int r = chunk * kMaxRowsPerCta + rg * kRowsPerWave + col;
-  const bool row_ok = wave_rows && r < a.rows;
-  const int i_row = row_ok ? r / a.G : 0;
-  const int gg = row_ok ? r - i_row * a.G : 0;
-
-  bf16x8 qreg[KS];
-  {
-    const uint16_t* qp = a.q + ((size_t(b) * a.K + i_row) * a.Hq + size_t(g) * a.G + gg) * D + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = *reinterpret_cast<const u32x4*>(qp + ks * 16);
-      qreg[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
-  // ---- tile loads: HBM -> LDS directly, 16 bytes per lane, 1 KiB per
-  // wavefront instruction.  Wavefront w loads tile rows 8w .. 8w+7 of K and
-  // of V: half of one cache page, whose id comes through the scalar cache.
+  // ---- where this wavefront's share of each tile comes from ---------------
+  // Wavefront w fetches tile rows 8w .. 8w+7 (half of page w/2) of K and V.
   // K rows keep granule c at c ^ (t % KG); V rows keep it at c ^ 2(t % (KG/2))
   // (granule pairs stay together for the transposing reads).
-  const cptr_i32 trow = (cptr_i32)(a.block_table) + size_t(b) * a.maxp;
-  const size_t page_stride = size_t(a.Hkv) * ORTHRUS_PAGE_SIZE * D;
+  const int32_t* trow = a.block_table + size_t(b) * a.maxp;
+  const size_t page_bytes = size_t(a.Hkv) * ORTHRUS_PAGE_SIZE * D * 2;
   const size_t blk_row = size_t(a.Hkv) * D;
   const int lrow = lane / KG;                    // row within one 1 KiB load
   const int lgran = lane % KG;                   // physical granule this lane fills
-  // byte offsets of this lane inside its half page (constant over tiles)
-  uint32_t koff[LPR], voff[LPR];
+  uint32_t koff[LPR], voff[LPR];                 // byte offsets inside the half page
   int trow_of[LPR];
 #pragma unroll
   for (int j = 0; j < LPR; ++j) {
@@ -205,11 +204,9 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   const uint16_t* kblk = a.k_blk + (size_t(b) * a.K * a.Hkv + g) * D;
   const uint16_t* vblk = a.v_blk + (size_t(b) * a.K * a.Hkv + g) * D;
 
-  auto issue_tile = [&](int ts, uint16_t* sbuf) {
-    const int pidx = min((ts >> 4) + (wave >> 1), a.maxp - 1);
-    const int page = min(max(trow[pidx], 0), a.num_pages - 1);
-    const char* kbase = kpool + size_t(page) * page_stride * 2;
-    const char* vbase = vpool + size_t(page) * page_stride * 2;
+  auto issue_tile = [&](int ts, int page, uint16_t* sbuf) {
+    const char* kbase = kpool + size_t(page) * page_bytes;
+    const char* vbase = vpool + size_t(page) * page_bytes;
     uint16_t* dst = sbuf + wave * LPR * 512;
     if (ts + kTile <= L) {                       // uniform: whole tile from the cache
 #pragma unroll
@@ -235,26 +232,54 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
       }
     }
   };
+  auto clamp_page = [&](int p) { return min(max(p, 0), a.num_pages - 1); };
+  auto page_index = [&](int t_idx) { return min((start >> 4) + 4 * t_idx + (wave >> 1), a.maxp - 1); };
+
+  // ---- prologue -------------------------------------------------------------
+  // The first NS-1 tiles go out first, with page ids read through the scalar
+  // cache; then the query rows and the page ids of the later tiles (vector
+  // loads, clamped only when used).  Vector loads complete in issue order, so
+  // the waits for the first tiles also cover q and the page ids.
+  {
+    const cptr_i32 strow = (cptr_i32)(a.block_table) + size_t(b) * a.maxp;
+    int pg0[NS - 1];
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k) pg0[k] = strow[page_index(k)];
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k)
+      if (k < ntiles) issue_tile(start + k * kTile, clamp_page(pg0[k]), stage_buf[k]);
+  }
+  const bool wave_rows = rg * kRowsPerWave < a.rpc;            // wave-uniform
+  const int r = chunk * kMaxRowsPerCta + rg * kRowsPerWave + col;
+  const bool row_ok = wave_rows && r < a.rows;
+  const int i_row = row_ok ? r / a.G : 0;
+  const int gg = row_ok ? r - i_row * a.G : 0;
+  u32x4 qraw[KS];
+  {
+    const uint16_t* qp = a.q + ((size_t(b) * a.K + i_row) * a.Hq + size_t(g) * a.G + gg) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qraw[ks] = u32x4{0u, 0u, 0u, 0u};
+      if (row_ok) qraw[ks] = *reinterpret_cast<const u32x4*>(qp + ks * 16);
+    }
+  }
+  int page_ids = 0;                              // lane i: this wavefront's page of tile i
+  if (lane < ntiles) page_ids = trow[page_index(lane)];
 
   // ---- running softmax state (per lane = per query row, this token half) --
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   // m_run is a lazily raised reference maximum (log2 units): it only moves
   // when a score exceeds it by more than 2^8, so P <= 256 and O is rarely
   // rescaled.  The result depends only on this row's own scores.
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_run = -__builtin_inff();
   float l_run = 0.f;
   const int row_limit = VERIFY ? (L + i_row) : (N - 1);  // last visible position
   const float c = a.scale_log2;
-
   const int trk = lane & 15;
   const int tr_dofs = 16 * ((lane >> 4) & 1) + 4 * (trk & 3);   // + db*32
   const int tr_tofs = 4 * half + (trk >> 2);                      // + th*32 + 16*k2 (+8)
-
-#pragma unroll
-  for (int k = 0; k < NS - 1; ++k)
-    if (k < ntiles) issue_tile(start + k * kTile, stage_buf[k]);
 
   for (int t0 = 0; t0 < ntiles; t0 += NS) {
 #pragma unroll
@@ -265,90 +290,97 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
       uint16_t* const sbuf = stage_buf[k];
       wait_tiles_outstanding<LPT>(min(NS - 2, ntiles - 1 - t));   // tile t has landed
       lds_barrier();                                               // ... for every wavefront
-      if (t + NS - 1 < ntiles) issue_tile(ts + (NS - 1) * kTile, stage_buf[(k + NS - 1) % NS]);
-        if (wave_rows) {
-          const uint16_t* ks = sbuf;
-          const uint16_t* vs = ks + TILE_ELEMS;
-          f32x16 sacc = f32x16{};
-          {
-            const int tok = th * 32 + col;
-            bf16x8 kf[KS];
-    #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-              const int gk = kk * 2 + half;
-              kf[kk] = *reinterpret_cast<const bf16x8*>(ks + tok * D + ((gk ^ (tok & (KG - 1))) * 8));
-            }
-    #pragma unroll
-            for (int kk = 0; kk < KS; ++kk)
-              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qreg[kk], sacc, 0, 0, 0);
-          }
-          // mask what this row may not see (raw scores; the scale is positive)
-          const int tok0 = ts + th * 32;
-          if (tok0 + 31 > row_limit) {
-    #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int pos = tok0 + 8 * (v >> 2) + 4 * half + (v & 3);
-              if (pos > row_limit) sacc[v] = -__builtin_inff();
-            }
-          }
-          float tmax = -__builtin_inff();
-    #pragma unroll
-          for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[v]);
-          tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c;
-          const float m_new = tmax > m_run + 8.0f ? tmax : m_run;
-          const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-          float lsum = 0.f;
-    #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c, -m_use));
-            sacc[v] = pv;
-            lsum += pv;
-          }
-          if (__any(m_new != m_run)) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            l_run *= alpha;
-    #pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-          }
-          l_run += lsum;
-          m_run = m_new;
+      if (t + NS - 1 < ntiles)
+        issue_tile(ts + (NS - 1) * kTile, clamp_page(__builtin_amdgcn_readlane(page_ids, t + NS - 1)),
+                   stage_buf[(k + NS - 1) % NS]);
 
-    #pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) {
-            bf16x8 pb;
-    #pragma unroll
-            for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(sacc[8 * k2 + j]);
-            const int t1 = th * 32 + 16 * k2 + tr_tofs;        // rows t1 and t1 + 8
-            const int sw = 2 * (t1 & (KG / 2 - 1));             // same for t1 + 8
-            bf16x8 vf[DB];
-    #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const int d = db * 32 + tr_dofs;
-              const int off = ((((d >> 3) ^ sw) * 8) + (d & 4));
-              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lptr_bf16x4)(vs + t1 * D + off));
-              const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lptr_bf16x4)(vs + (t1 + 8) * D + off));
-              vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-    #pragma unroll
-            for (int db = 0; db < DB; ++db)
-              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb, oacc[db], 0, 0, 0);
+      if (wave_rows) {
+        const uint16_t* ks = sbuf;
+        const uint16_t* vs = sbuf + TILE_ELEMS;
+        f32x16 sacc = f32x16{};
+        {
+          const int tok = th * 32 + col;
+          bf16x8 kf[KS];
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) {
+            const int gk = kk * 2 + half;
+            kf[kk] = *reinterpret_cast<const bf16x8*>(ks + tok * D + ((gk ^ (tok & (KG - 1))) * 8));
+          }
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], __builtin_bit_cast(bf16x8, qraw[kk]),
+                                                           sacc, 0, 0, 0);
+        }
+        // mask what this row may not see (raw scores; the scale is positive)
+        const int tok0 = ts + th * 32;
+        if (tok0 + 31 > row_limit) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int pos = tok0 + 8 * (v >> 2) + 4 * half + (v & 3);
+            if (pos > row_limit) sacc[v] = -__builtin_inff();
           }
         }
+        float tmax = -__builtin_inff();
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[v]);
+        tmax = xor32_max(tmax) * c;
+        const float m_new = tmax > m_run + 8.0f ? tmax : m_run;
+        const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+        float lsum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c, -m_use));
+          sacc[v] = pv;
+          lsum += pv;
+        }
+        if (__any(m_new != m_run)) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        }
+        l_run += lsum;
+        m_run = m_new;
+
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          bf16x8 pb;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(sacc[8 * k2 + j]);
+          const int t1 = th * 32 + 16 * k2 + tr_tofs;        // rows t1 and t1 + 8
+          const int sw = 2 * (t1 & (KG / 2 - 1));             // same for t1 + 8
+          bf16x8 vf[DB];
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int d = db * 32 + tr_dofs;
+            const int off = ((((d >> 3) ^ sw) * 8) + (d & 4));
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lptr_bf16x4)(vs + t1 * D + off));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lptr_bf16x4)(vs + (t1 + 8) * D + off));
+            vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb, oacc[db], 0, 0, 0);
+        }
+      }
     }
   }
 
   // ---- merge the two token halves of each row group through LDS ----------
-  l_run += __shfl_xor(l_run, 32);
+  l_run = xor32_sum(l_run);
   lds_barrier();                                   // every wavefront is done with the ring
+  // rows padded by 4 floats: lane col writes row col, and the padding puts
+  // consecutive rows on different LDS banks
+  constexpr int XS = D + 4;
   float* xo = reinterpret_cast<float*>(rg == 0 ? st0 : rg == 1 ? st1 : rg == 2 ? st2 : st3);
-  float* xml = xo + kRowsPerWave * D;
+  float* xml = xo + kRowsPerWave * XS;
   if (wave_rows && th == 1) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f32x4 o4 = {oacc[db][4 * j + 0], oacc[db][4 * j + 1], oacc[db][4 * j + 2], oacc[db][4 * j + 3]};
-        *reinterpret_cast<f32x4*>(xo + col * D + db * 32 + 8 * j + 4 * half) = o4;
+        *reinterpret_cast<f32x4*>(xo + col * XS + db * 32 + 8 * j + 4 * half) = o4;
       }
     if (half == 0) {
       xml[col] = m_run;
@@ -363,47 +395,46 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   const float M_use = (M == -__builtin_inff()) ? 0.f : M;
   const float wa = __builtin_amdgcn_exp2f(m_run - M_use);
   const float wb = __builtin_amdgcn_exp2f(m_b - M_use);
+  const float l_tot = wa * l_run + wb * l_b;
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   const size_t part = ((size_t(b) * a.Hkv + g) * a.nchunks + chunk) * a.nsplit + s;
   const size_t prow = part * a.rpc + rg * kRowsPerWave + col;
-  float* po = a.part_o + prow * D;
+  uint16_t* po = a.part_o + prow * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f32x4 ob = *reinterpret_cast<const f32x4*>(xo + col * D + db * 32 + 8 * j + 4 * half);
-      f32x4 o4;
+      const f32x4 ob = *reinterpret_cast<const f32x4*>(xo + col * XS + db * 32 + 8 * j + 4 * half);
+      float o[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o4[i] = wa * oacc[db][4 * j + i] + wb * ob[i];
-      *reinterpret_cast<f32x4*>(po + db * 32 + 8 * j + 4 * half) = o4;
+      for (int i = 0; i < 4; ++i) o[i] = (wa * oacc[db][4 * j + i] + wb * ob[i]) * inv;
+      const u32x2 w2 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      *reinterpret_cast<u32x2*>(po + db * 32 + 8 * j + 4 * half) = w2;
     }
   if (half == 0) {
     a.part_ml[prow * 2 + 0] = M;
-    a.part_ml[prow * 2 + 1] = wa * l_run + wb * l_b;
+    a.part_ml[prow * 2 + 1] = l_tot;
   }
 }
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;  // NaN stays NaN
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // Merge the split partials of every output row:
-//   out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
-// One wavefront per output row: D/4 lanes cover the row (4 values each) and
-// the 64/(D/4) lane groups take interleaved splits s = group, group + SG, ...
-// in increasing order; the group sums are then added in group order.  Splits
-// a row cannot see contribute exact zeros, so the result does not depend on
-// how many splits the call had.
+//   out = sum_s w_s l_s Ohat_s / sum_s w_s l_s,  w_s = 2^(m_s - M),  M = max_s m_s,
+// with Ohat_s = O_s / l_s (bf16).  One wavefront per output row: lane s % 64
+// reads split s's (m, l); D/8 lanes cover the row (8 values, 16 bytes each)
+// and the 64/(D/8) lane groups take interleaved splits in increasing order,
+// four loads in flight per lane; the group sums are added in group order.
+// Splits a row cannot see contribute exact zeros, so the result does not
+// depend on how many splits the call had.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
-  constexpr int TPR = D / 4;      // lanes per row slice
+  constexpr int TPR = D / 8;      // lanes per row slice
   constexpr int SG = 64 / TPR;    // split groups per wavefront
+  constexpr int U = 4;            // splits in flight per lane group
   const int lane = threadIdx.x & 63;
   const int orow = blockIdx.x * 4 + (threadIdx.x >> 6);   // (b, i, h) flattened
   if (orow >= a.B * a.K * a.Hq) return;                    // uniform per wavefront
   const int sg = lane / TPR;
-  const int d0 = (lane % TPR) * 4;
+  const int d0 = (lane % TPR) * 8;
   const int h = orow % a.Hq;
   const int bi = orow / a.Hq;
   const int i = bi % a.K;
@@ -417,40 +448,62 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
   const int Hkv = a.Hq / a.G;
   const size_t prow0 = ((size_t(b) * Hkv + g) * a.nchunks + chunk) * a.nsplit * a.rpc + rl;
   const float* ml = a.part_ml + prow0 * 2;
-  const float* po = a.part_o + prow0 * D + d0;
+  const uint16_t* po = a.part_o + prow0 * D + d0;
   const size_t ml_stride = size_t(a.rpc) * 2, o_stride = size_t(a.rpc) * D;
 
   float M = -__builtin_inff();
-#pragma unroll 4
-  for (int s = sg; s < ns; s += SG) M = fmaxf(M, ml[s * ml_stride]);
+  for (int s0 = 0; s0 < ns; s0 += 64)
+    if (s0 + lane < ns) M = fmaxf(M, ml[(s0 + lane) * ml_stride]);
 #pragma unroll
-  for (int off = TPR; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float M_use = (M == -__builtin_inff()) ? 0.f : M;
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-#pragma unroll 4
-  for (int s = sg; s < ns; s += SG) {
-    const float w = __builtin_amdgcn_exp2f(ml[s * ml_stride] - M);
-    const f32x4 o = *reinterpret_cast<const f32x4*>(po + s * o_stride);
-    acc += w * o;
-    lsum += w * ml[s * ml_stride + 1];
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    float wl = 0.f;                                   // w_s * l_s of split s0 + lane
+    if (s0 + lane < ns) {
+      const float* e = ml + (s0 + lane) * ml_stride;
+      wl = __builtin_amdgcn_exp2f(e[0] - M_use) * e[1];
+    }
+    const int cnt = min(64, ns - s0);
+    for (int jj = 0; jj < cnt; jj += U * SG) {
+      u32x4 raw[U];
+      float w[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = jj + u * SG + sg;               // this lane group's split
+        w[u] = __shfl(wl, j & 63);
+        raw[u] = u32x4{0u, 0u, 0u, 0u};
+        if (j < cnt) raw[u] = *reinterpret_cast<const u32x4*>(po + (s0 + j) * o_stride);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (jj + u * SG + sg < cnt) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += w[u] * bf16_lo(raw[u][q]);
+            acc[2 * q + 1] += w[u] * bf16_hi(raw[u][q]);
+          }
+          lsum += w[u];
+        }
+      }
+    }
   }
-  f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+  float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float ltot = 0.f;
 #pragma unroll
   for (int k = 0; k < SG; ++k) {
     const int src = (lane % TPR) + k * TPR;
-    tot[0] += __shfl(acc[0], src);
-    tot[1] += __shfl(acc[1], src);
-    tot[2] += __shfl(acc[2], src);
-    tot[3] += __shfl(acc[3], src);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) tot[q] += __shfl(acc[q], src);
     ltot += __shfl(lsum, src);
   }
   if (sg != 0) return;
   const float inv = 1.0f / ltot;
-  u32x2 packed = {bf16_rne_bits(tot[0] * inv) | (bf16_rne_bits(tot[1] * inv) << 16),
-                  bf16_rne_bits(tot[2] * inv) | (bf16_rne_bits(tot[3] * inv) << 16)};
-  *reinterpret_cast<u32x2*>(a.out + size_t(orow) * D + d0) = packed;
+  const u32x4 packed = {pack_bf16x2(tot[0] * inv, tot[1] * inv), pack_bf16x2(tot[2] * inv, tot[3] * inv),
+                        pack_bf16x2(tot[4] * inv, tot[5] * inv), pack_bf16x2(tot[6] * inv, tot[7] * inv)};
+  *reinterpret_cast<u32x4*>(a.out + size_t(orow) * D + d0) = packed;
 }
 
 template <int D, bool VERIFY>
@@ -472,7 +525,7 @@ hipError_t launch_attention(const AttnPlan& p, const orthrus_kv& kv, const void*
   a.q = static_cast<const uint16_t*>(q);
   a.k_blk = static_cast<const uint16_t*>(k_blk);
   a.v_blk = static_cast<const uint16_t*>(v_blk);
-  a.part_o = static_cast<float*>(ws);
+  a.part_o = static_cast<uint16_t*>(ws);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_o_bytes);
   a.B = p.B; a.K = p.K; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G;
   a.num_pages = kv.num_pages; a.maxp = kv.max_pages_per_seq; a.max_ctx = p.max_ctx;

@@ -54,7 +54,7 @@ int attn_split_tokens(int B, int Hkv, int max_ctx) {
   const int64_t target = B == 1 ? 256 : 1024;
   int64_t s = round_up(ceil_div(work, target), kTile);
   if (s < 2 * kTile) s = 2 * kTile;
-  if (s > 1024 * kTile) s = 1024 * kTile;
+  if (s > kMaxSplitTiles * kTile) s = kMaxSplitTiles * kTile;
   return int(s);
 }
 
@@ -67,7 +67,8 @@ bool plan_attention_shape(int B, int K, int Hq, int Hkv, int D, int max_ctx, int
   if (Hq / Hkv > kMaxGroup) return no("group size num_q_heads/num_kv_heads must be <= 16");
   if (D != 64 && D != 128) return no("head_dim must be 64 or 128");
   if (max_ctx < 0 || max_ctx > (1 << 30)) return no("max_ctx out of range");
-  if (split_tokens < 0 || split_tokens % kTile) return no("split_tokens must be 0 or a positive multiple of 64");
+  if (split_tokens < 0 || split_tokens % kTile || split_tokens > kMaxSplitTiles * kTile)
+    return no("split_tokens must be 0 or a multiple of 64 up to 4096");
   p->B = B; p->K = K; p->Hq = Hq; p->Hkv = Hkv; p->G = Hq / Hkv; p->D = D;
   p->max_ctx = max_ctx;
   p->split = split_tokens ? split_tokens : attn_split_tokens(B, Hkv, max_ctx);
@@ -76,7 +77,7 @@ bool plan_attention_shape(int B, int K, int Hq, int Hkv, int D, int max_ctx, int
   p->nchunks = int(ceil_div(p->rows, kMaxRowsPerCta));
   p->rows_per_chunk = p->rows > kMaxRowsPerCta ? kMaxRowsPerCta : int(round_up(p->rows, kRowsPerWave));
   const int64_t parts = int64_t(B) * Hkv * p->nchunks * p->nsplit * p->rows_per_chunk;
-  p->part_o_bytes = size_t(round_up(parts * D * 4, 256));
+  p->part_o_bytes = size_t(round_up(parts * D * 2, 256));   // bf16 O / l per split row
   p->part_ml_bytes = size_t(round_up(parts * 2 * 4, 256));
   p->ws_bytes = p->part_o_bytes + p->part_ml_bytes;
   return true;
@@ -91,7 +92,8 @@ int check_attention(const orthrus_kv* kv, const void* q, const void* k_blk, cons
   std::string why;
   if (!plan_attention_shape(B, K, Hq, kv->num_kv_heads, kv->head_dim, max_ctx, split_tokens, plan, &why)) {
     if (err) *err = why;
-    return (B < 0 || max_ctx < 0 || split_tokens < 0 || split_tokens % kTile)
+    return (B < 0 || max_ctx < 0 || split_tokens < 0 || split_tokens % kTile ||
+            split_tokens > kMaxSplitTiles * kTile)
                ? ORTHRUS_ERR_INVALID_ARG : ORTHRUS_ERR_UNSUPPORTED_SHAPE;
   }
   if (!(std::isfinite(scale) && scale > 0.f))

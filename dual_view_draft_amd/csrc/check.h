@@ -15,6 +15,7 @@ constexpr int kTile = 64;          // tokens per attention tile (4 pages)
 constexpr int kRowsPerWave = 32;   // query rows per wavefront (one 32x32 MFMA block)
 constexpr int kMaxRowsPerCta = 128;
 constexpr int kMaxGroup = 16;
+constexpr int kMaxSplitTiles = 64;  // a context split covers at most 64 tiles (4096 tokens)
 
 // Geometry of one attention call, all derived on the host.
 struct AttnPlan {

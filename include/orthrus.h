@@ -140,7 +140,7 @@ ORTHRUS_API size_t orthrus_attn_workspace_bytes(int batch, int block_k, int num_
  *  scale        : score scale, normally 1/sqrt(head_dim); finite, > 0
  *  max_ctx      : host-known upper bound on every L_b (sizes the grid; no
  *                 device->host read is needed).  L_b > max_ctx is clamped.
- *  split_tokens : context split size (multiple of 64), 0 = automatic
+ *  split_tokens : context split size (multiple of 64, at most 4096), 0 = automatic
  *  workspace    : device scratch of >= orthrus_attn_workspace_bytes(...) bytes,
  *                 16-byte aligned; contents on entry do not matter.
  *

@@ -57,7 +57,7 @@ def test_workspace_queries(lib):
     split = lib.orthrus_attn_split_tokens(1, 8, 40960)
     assert split % 64 == 0 and split > 0
     nsplit = -(-(40960 + 32) // split)
-    assert n >= nsplit * 8 * 128 * (128 + 2) * 4
+    assert n >= nsplit * 8 * 128 * (128 * 2 + 2 * 4)
     assert lib.orthrus_attn_workspace_bytes(1, 65, 32, 8, 128, 100, 0) == 0
     assert lib.orthrus_attn_workspace_bytes(1, 32, 32, 8, 96, 100, 0) == 0
     assert lib.orthrus_argmax_workspace_bytes(32, 151936) >= 32 * 8
