@@ -49,7 +49,11 @@ def parse_args():
     p.add_argument("--pools", type=int, default=0, help="KV pool copies to rotate (0 = auto)")
     p.add_argument("--split", type=int, default=0, help="split_tokens override (0 = library choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", dest="graph", action="store_false",
+                   help="launch the timed steps eagerly instead of replaying HIP graphs")
     p.add_argument("--cpu-steps", type=int, default=3)
+    p.add_argument("--quick", action="store_true",
+                   help="timed steps only (no per-op breakdown, no CPU baseline): for profiler runs")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -70,7 +74,7 @@ def measured_traffic(kv_bytes_per_launch: float):
         return None
     if t.get("attn_source_sha256_16") != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_split_launch")
+    return t.get("hbm_bytes_per_attention_call")
 
 
 def setup(args, torch, dv, synth):
@@ -152,24 +156,17 @@ def main():
     kb_commit, vb_commit = kb_v[None], vb_v[None]
     torch.cuda.synchronize()
 
-    ops = ["draft_attn", "draft_argmax", "verify_attn", "accept", "commit"]
-
-    def step(i, ev=None):
+    def step(i):
         kv = kvs[(2 * i) % n_pools]           # draft and verify read different pool copies,
         kv_v = kvs[(2 * i + 1) % n_pools]     # as a real model's two passes are layers apart
-        if ev: ev[0].record(stream)
+        s_ = torch.cuda.current_stream()      # the capture stream while a graph is recorded
         dv.orthrus_attn_draft(kv, q_d, kb_d, vb_d, out_d, max_ctx=max_ctx, split_tokens=args.split,
-                              workspace=ws_attn, stream=stream)
-        if ev: ev[1].record(stream)
-        dv.orthrus_argmax(logits_d, d_tok, workspace=ws_arg, stream=stream)
-        if ev: ev[2].record(stream)
+                              workspace=ws_attn, stream=s_)
+        dv.orthrus_argmax(logits_d, d_tok, workspace=ws_arg, stream=s_)
         dv.orthrus_attn_verify(kv_v, q_v, kb_v, vb_v, out_v, max_ctx=max_ctx, split_tokens=args.split,
-                               workspace=ws_attn, stream=stream)
-        if ev: ev[3].record(stream)
-        dv.orthrus_accept(logits_a, d_tok, a_tok, n_acc, n_emit, nxt, workspace=ws_arg, stream=stream)
-        if ev: ev[4].record(stream)
-        dv.orthrus_commit_kv(kv_v, kb_commit, vb_commit, n_emit, lens_out, stream=stream)
-        if ev: ev[5].record(stream)
+                               workspace=ws_attn, stream=s_)
+        dv.orthrus_accept(logits_a, d_tok, a_tok, n_acc, n_emit, nxt, workspace=ws_arg, stream=s_)
+        dv.orthrus_commit_kv(kv_v, kb_commit, vb_commit, n_emit, lens_out, stream=s_)
 
     for i in range(args.warmup):
         step(i)
@@ -177,30 +174,71 @@ def main():
     # sanity: the consensus reproduces the drawn accepted lengths
     assert torch.equal(n_acc.cpu(), torch.from_numpy(cons.n_acc)), "accept mismatch"
 
-    # ---- timed region: plain steps, whole-job clock --------------------------
+    def capture(fn):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        return graph
+
+    # ---- timed region ------------------------------------------------------------
+    # Each step is replayed from a HIP graph of the same five library calls, so
+    # the GPU runs the kernels back to back without host gaps.  Draft and
+    # verify read different pool copies; the graphs cycle through the copies.
+    n_graphs = max(1, n_pools // 2) if args.graph else 0
+    graphs = [capture(lambda j=j: step(j)) for j in range(n_graphs)]
+    torch.cuda.synchronize()
+    for j in range(n_graphs):                      # one warm replay each
+        graphs[j].replay()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(args.steps):
-        step(i)
+        if args.graph:
+            graphs[i % n_graphs].replay()
+        else:
+            step(i)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    # ---- per-op breakdown (separate pass, events between the calls) ----------
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    per_op = {op: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, op in enumerate(ops)}
-    op_ms = {op: statistics.mean(v) for op, v in per_op.items()}
-    op_med = {op: statistics.median(v) for op, v in per_op.items()}
+    # ---- per-op device time: graphs of REPS back-to-back calls of one op ----
+    REPS = 16
+    op_calls = {
+        "draft_attn": lambda i: dv.orthrus_attn_draft(kvs[(2 * i) % n_pools], q_d, kb_d, vb_d, out_d,
+                                                      max_ctx=max_ctx, split_tokens=args.split,
+                                                      workspace=ws_attn, stream=None),
+        "draft_argmax": lambda i: dv.orthrus_argmax(logits_d, d_tok, workspace=ws_arg, stream=None),
+        "verify_attn": lambda i: dv.orthrus_attn_verify(kvs[(2 * i + 1) % n_pools], q_v, kb_v, vb_v, out_v,
+                                                        max_ctx=max_ctx, split_tokens=args.split,
+                                                        workspace=ws_attn, stream=None),
+        "accept": lambda i: dv.orthrus_accept(logits_a, d_tok, a_tok, n_acc, n_emit, nxt,
+                                              workspace=ws_arg, stream=None),
+        "commit": lambda i: dv.orthrus_commit_kv(kvs[(2 * i + 1) % n_pools], kb_commit, vb_commit, n_emit,
+                                                 lens_out, stream=None),
+    }
+    op_ms, op_min = {}, {}
+    for op, call in ([] if args.quick else op_calls.items()):
+        graph = capture(lambda call=call: [call(i) for i in range(REPS)])
+        graph.replay()
+        samples = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            samples.append(e0.elapsed_time(e1) / REPS)
+        op_ms[op] = statistics.median(samples)
+        op_min[op] = min(samples)
+    op_med = op_ms
 
     # ---- algorithmic bytes / flops per attention launch ----------------------
     pages_read = sum(-(-l // 16) for l in L)
     attn_bytes = (kv_bytes + 2 * B * K * Hq * D * 2 + 2 * 2 * B * K * Hkv * D * 2 + 4 * pages_read + 4 * B)
     attn_flops = 4.0 * Hq * K * D * sum(l + K for l in L)
+    if args.quick:
+        print(json.dumps({"ms_per_step": round(ms_per_step, 4), "steps": args.steps}), flush=True)
+        return
     dom = max(("draft_attn", "verify_attn"), key=lambda o: op_ms[o])
     dom_s = op_ms[dom] * 1e-3
     achieved = attn_bytes / dom_s / 1e9
@@ -228,12 +266,12 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "steps_per_s": round(1e3 / ms_per_step, 1),
         "tokens_per_step_expected": round(float(sum(min(int(a) + 1, K) for a in cons.n_acc)), 2),
-        "op_ms_mean": {k: round(v, 4) for k, v in op_ms.items()},
-        "op_ms_median": {k: round(v, 4) for k, v in op_med.items()},
+        "op_ms": {k: round(v, 4) for k, v in op_ms.items()},
+        "timing": "HIP graph replay" if args.graph else "eager launches",
         "attn_kv_gbps": {o: round(kv_bytes / (op_ms[o] * 1e-3) / 1e9, 1)
                          for o in ("draft_attn", "verify_attn")},
         "roofline": {
-            "kernel": f"{dom} (attn_split_kernel + attn_combine_kernel)",
+            "kernel": f"{dom}: attn_split_kernel + attn_combine_kernel (one ABI call)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

@@ -81,6 +81,7 @@ __device__ __forceinline__ int32_t key_index(unsigned long long k) {
 }
 
 __global__ __launch_bounds__(256) void argmax_partial_kernel(PartialArgs a) {
+  constexpr int UNR = 4;                         // float4 loads in flight per thread
   __shared__ unsigned long long red[4];
   const int row = blockIdx.y;
   const int c = blockIdx.x;
@@ -90,13 +91,25 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(PartialArgs a) {
   unsigned long long best = 0ull;
   if ((a.V & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0) {
     const f32x4* b4 = reinterpret_cast<const f32x4*>(base);
-    for (int v4 = (lo >> 2) + threadIdx.x; v4 < (hi >> 2); v4 += 256) {
-      const f32x4 x = b4[v4];
-      const int v = v4 * 4;
-      best = umax64(best, make_key(x[0], v));
-      best = umax64(best, make_key(x[1], v + 1));
-      best = umax64(best, make_key(x[2], v + 2));
-      best = umax64(best, make_key(x[3], v + 3));
+    const int hi4 = hi >> 2;
+    for (int v0 = (lo >> 2) + threadIdx.x; v0 < hi4; v0 += 256 * UNR) {
+      f32x4 x[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int v4 = v0 + u * 256;
+        x[u] = v4 < hi4 ? b4[v4] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int v4 = v0 + u * 256;
+        if (v4 < hi4) {
+          const int v = v4 * 4;
+          best = umax64(best, make_key(x[u][0], v));
+          best = umax64(best, make_key(x[u][1], v + 1));
+          best = umax64(best, make_key(x[u][2], v + 2));
+          best = umax64(best, make_key(x[u][3], v + 3));
+        }
+      }
     }
   } else {
     for (int v = lo + threadIdx.x; v < hi; v += 256) best = umax64(best, make_key(base[v], v));
@@ -110,25 +123,42 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(PartialArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void argmax_final_kernel(FinalArgs a) {
-  const int row = blockIdx.x * 256 + threadIdx.x;
-  if (row >= a.rows) return;
+// Reduce the chunk keys of one row with one wavefront (lane c reads chunk c).
+__device__ __forceinline__ unsigned long long row_key(const unsigned long long* keys, int nchunks, int lane) {
   unsigned long long best = 0ull;
-  for (int c = 0; c < a.nchunks; ++c) best = umax64(best, a.keys[size_t(row) * a.nchunks + c]);
-  a.out[row] = key_index(best);
+  for (int c = lane; c < nchunks; c += 64) best = umax64(best, keys[c]);
+  return wave_max(best);
 }
 
-// One wavefront per sequence; lane i owns block row i (K <= 64).
-__global__ __launch_bounds__(64) void accept_kernel(AcceptArgs a) {
+// One wavefront per row.
+__global__ __launch_bounds__(256) void argmax_final_kernel(FinalArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;                     // uniform per wavefront
+  const int lane = threadIdx.x & 63;
+  const unsigned long long best = row_key(a.keys + size_t(row) * a.nchunks, a.nchunks, lane);
+  if (lane == 0) a.out[row] = key_index(best);
+}
+
+// One workgroup per sequence: its four wavefronts reduce the K rows' chunk
+// keys (rows w, w+4, ...), then wavefront 0 runs the prefix scan with lane i
+// owning block row i (K <= 64).
+__global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
+  __shared__ int32_t tok_s[64];
   const int b = blockIdx.x;
-  const int i = threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int i = w; i < a.K; i += 4) {
+    const size_t row = size_t(b) * a.K + i;
+    const unsigned long long best = row_key(a.keys + row * a.nchunks, a.nchunks, lane);
+    if (lane == 0) tok_s[i] = key_index(best);
+  }
+  __syncthreads();
+  if (w != 0) return;
+  const int i = lane;
   int32_t tok = 0;
   bool mismatch = false;
   if (i < a.K) {
     const size_t row = size_t(b) * a.K + i;
-    unsigned long long best = 0ull;
-    for (int c = 0; c < a.nchunks; ++c) best = umax64(best, a.keys[row * a.nchunks + c]);
-    tok = key_index(best);
+    tok = tok_s[i];
     a.a[row] = tok;
     mismatch = a.draft[row] != tok;
   }
@@ -155,7 +185,7 @@ hipError_t launch_argmax(const ArgmaxPlan& p, const float* logits, int32_t* out,
   hipError_t e = launch_partial(p, logits, ws, stream);
   if (e != hipSuccess) return e;
   FinalArgs f{static_cast<const unsigned long long*>(ws), out, p.rows, p.nchunks};
-  return launch_kernel(&argmax_final_kernel, dim3((p.rows + 255) / 256), dim3(256), stream, f);
+  return launch_kernel(&argmax_final_kernel, dim3((p.rows + 3) / 4), dim3(256), stream, f);
 }
 
 hipError_t launch_accept(const ArgmaxPlan& p, const float* logits_a, const int32_t* draft, int B,
@@ -165,7 +195,7 @@ hipError_t launch_accept(const ArgmaxPlan& p, const float* logits_a, const int32
   if (e != hipSuccess) return e;
   AcceptArgs x{static_cast<const unsigned long long*>(ws), draft, a, n_acc, n_emit, next_anchor,
                B, K, p.nchunks};
-  return launch_kernel(&accept_kernel, dim3(B), dim3(64), stream, x);
+  return launch_kernel(&accept_kernel, dim3(B), dim3(256), stream, x);
 }
 
 }  // namespace orthrus
