@@ -51,6 +51,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef const int32_t __attribute__((address_space(4)))* cptr_i32;
@@ -126,19 +127,31 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-// Wait until at most n * PER vector-memory instructions of this wavefront are
-// outstanding (n uniform, 0..2).  Vector loads complete in issue order.
-template <int PER>
-__device__ __forceinline__ void wait_tiles_outstanding(int n) {
-  if (n >= 2) wait_vmcnt<2 * PER>();
-  else if (n == 1) wait_vmcnt<PER>();
-  else wait_vmcnt<0>();
+// Global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane l's
+// bytes land at LDS byte address lds + 16 l.  It is written as assembly so
+// that the compiler does not track these LDS writes: lacking proof that a
+// later LDS read touches another ring stage, it would wait for every load in
+// flight before that read, draining the ring.  The ring's own vmcnt waits
+// and barriers order each read after the loads that fill its stage.
+__device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(lds), "v"(src)
+      : "memory", "m0");
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lptr_void)(p)));
 }
 
 template <int D>
 struct SplitCfg {
   static constexpr int KG = D / 8;                 // 16-byte granules per key/value row
-  static constexpr int NS = 4;                     // LDS ring stages
+  static constexpr int NS = 5;                     // LDS ring stages
   static constexpr int TILE_ELEMS = kTile * D;     // bf16 values per K (or V) tile
   static constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;
   static constexpr int RPI = 512 / D;              // tile rows per 1 KiB wave-wide LDS load
@@ -156,12 +169,13 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   // One array per ring stage, always indexed with compile-time stage numbers:
   // the compiler can then tell that reading one stage does not depend on the
   // DMA still writing another, and inserts no wait for it.
-  static_assert(NS == 4, "ring of four stages");
+  static_assert(NS == 4 || NS == 5, "ring of four or five stages");
   __shared__ __attribute__((aligned(16))) uint16_t st0[STAGE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t st1[STAGE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t st2[STAGE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t st3[STAGE_ELEMS];
-  uint16_t* const stage_buf[NS] = {st0, st1, st2, st3};
+  __shared__ __attribute__((aligned(16))) uint16_t st4[NS == 5 ? STAGE_ELEMS : 8];
+  uint16_t* const stage_buf[5] = {st0, st1, st2, st3, st4};
 
   const int s = blockIdx.x;
   const int g = blockIdx.y / a.nchunks;
@@ -172,9 +186,53 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
   const int rg = wave & 3, th = wave >> 2;      // row group, token half
 
-  const int L = clamp_len(a.seq_lens[b], a.max_ctx);
-  const int N = L + a.K;                         // keys that exist for this sequence
   const int start = s * a.split;
+  // Table index of this wavefront's page of tile t_idx, clamped to the row so
+  // it can be read before the sequence length is known.
+  auto page_index = [&](int t_idx) { return min((start >> 4) + 4 * t_idx + (wave >> 1), a.maxp - 1); };
+  const int32_t* trow = a.block_table + size_t(b) * a.maxp;
+
+  // ---- prologue, part 1: one memory round trip ---------------------------
+  // Scalar loads: the sequence length and the page ids of the first NS-1
+  // tiles.  Vector loads: the page ids of every tile of the split (lane i:
+  // tile i, clamped only when used) and this lane's query row.  All of them
+  // are waited for before any tile load is issued: a register value still in
+  // flight when the tile loop starts makes the compiler drain the whole
+  // memory queue, tile loads included, at the loop entry.
+  int pg0[NS - 1];
+  int L_raw;
+  {
+    const cptr_i32 strow = (cptr_i32)(a.block_table) + size_t(b) * a.maxp;
+    L_raw = ((cptr_i32)(a.seq_lens))[b];
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k) pg0[k] = strow[page_index(k)];
+  }
+  static_assert(kMaxSplitTiles <= 64, "one lane per tile of a split");
+  const int page_ids = trow[page_index(lane)];   // lane i: this wavefront's page of tile i
+  const bool wave_rows = rg * kRowsPerWave < a.rpc;            // wave-uniform
+  const int r = chunk * kMaxRowsPerCta + rg * kRowsPerWave + col;
+  const bool row_ok = wave_rows && r < a.rows;
+  const int i_row = row_ok ? r / a.G : 0;
+  const int gg = row_ok ? r - i_row * a.G : 0;
+  u32x4 qraw[KS];
+  {
+    const uint16_t* qp = a.q + ((size_t(b) * a.K + i_row) * a.Hq + size_t(g) * a.G + gg) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qraw[ks] = u32x4{0u, 0u, 0u, 0u};
+      if (row_ok) qraw[ks] = *reinterpret_cast<const u32x4*>(qp + ks * 16);
+    }
+  }
+  // The empty asm takes the scalar results as operands and clobbers memory:
+  // the compiler can move none of these loads past it, so all of them are in
+  // flight together before the single wait below.
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k) asm volatile("" ::"s"(pg0[k]));
+  asm volatile("" ::"s"(L_raw) : "memory");
+  __builtin_amdgcn_s_waitcnt(0);                 // vmcnt(0) expcnt(0) lgkmcnt(0)
+
+  const int L = clamp_len(L_raw, a.max_ctx);
+  const int N = L + a.K;                         // keys that exist for this sequence
   if (start >= N) return;                        // uniform across the workgroup
   const int end = min(start + a.split, N);
   const int ntiles = (end - start + kTile - 1) / kTile;   // <= kMaxSplitTiles
@@ -183,7 +241,6 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   // Wavefront w fetches tile rows 8w .. 8w+7 (half of page w/2) of K and V.
   // K rows keep granule c at c ^ (t % KG); V rows keep it at c ^ 2(t % (KG/2))
   // (granule pairs stay together for the transposing reads).
-  const int32_t* trow = a.block_table + size_t(b) * a.maxp;
   const size_t page_bytes = size_t(a.Hkv) * ORTHRUS_PAGE_SIZE * D * 2;
   const size_t blk_row = size_t(a.Hkv) * D;
   const int lrow = lane / KG;                    // row within one 1 KiB load
@@ -211,9 +268,8 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
     if (ts + kTile <= L) {                       // uniform: whole tile from the cache
 #pragma unroll
       for (int j = 0; j < LPR; ++j) {
-        __builtin_amdgcn_global_load_lds((gptr_void)(kbase + koff[j]), (lptr_void)(dst + j * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gptr_void)(vbase + voff[j]),
-                                         (lptr_void)(dst + TILE_ELEMS + j * 512), 16, 0, 0);
+        load_lds16(kbase + koff[j], lds_addr(dst + j * 512));
+        load_lds16(vbase + voff[j], lds_addr(dst + TILE_ELEMS + j * 512));
       }
     } else {
 #pragma unroll
@@ -227,44 +283,30 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
           ks = p < N ? static_cast<const void*>(kblk + (p - L) * blk_row + ck * 8) : g_zero16;
           vs = p < N ? static_cast<const void*>(vblk + (p - L) * blk_row + cv * 8) : g_zero16;
         }
-        __builtin_amdgcn_global_load_lds((gptr_void)ks, (lptr_void)(dst + j * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gptr_void)vs, (lptr_void)(dst + TILE_ELEMS + j * 512), 16, 0, 0);
+        load_lds16(ks, lds_addr(dst + j * 512));
+        load_lds16(vs, lds_addr(dst + TILE_ELEMS + j * 512));
       }
     }
   };
-  auto clamp_page = [&](int p) { return min(max(p, 0), a.num_pages - 1); };
-  auto page_index = [&](int t_idx) { return min((start >> 4) + 4 * t_idx + (wave >> 1), a.maxp - 1); };
-
-  // ---- prologue -------------------------------------------------------------
-  // The first NS-1 tiles go out first, with page ids read through the scalar
-  // cache; then the query rows and the page ids of the later tiles (vector
-  // loads, clamped only when used).  Vector loads complete in issue order, so
-  // the waits for the first tiles also cover q and the page ids.
-  {
-    const cptr_i32 strow = (cptr_i32)(a.block_table) + size_t(b) * a.maxp;
-    int pg0[NS - 1];
+  // A tile past the end of the split: the same number of loads, all from the
+  // 16 zero bytes, so that every step of the ring issues the same count and
+  // the waits below are fixed numbers.
+  auto issue_dummy = [&](uint16_t* sbuf) {
+    uint16_t* dst = sbuf + wave * LPR * 512;
 #pragma unroll
-    for (int k = 0; k < NS - 1; ++k) pg0[k] = strow[page_index(k)];
-#pragma unroll
-    for (int k = 0; k < NS - 1; ++k)
-      if (k < ntiles) issue_tile(start + k * kTile, clamp_page(pg0[k]), stage_buf[k]);
-  }
-  const bool wave_rows = rg * kRowsPerWave < a.rpc;            // wave-uniform
-  const int r = chunk * kMaxRowsPerCta + rg * kRowsPerWave + col;
-  const bool row_ok = wave_rows && r < a.rows;
-  const int i_row = row_ok ? r / a.G : 0;
-  const int gg = row_ok ? r - i_row * a.G : 0;
-  u32x4 qraw[KS];
-  {
-    const uint16_t* qp = a.q + ((size_t(b) * a.K + i_row) * a.Hq + size_t(g) * a.G + gg) * D + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qraw[ks] = u32x4{0u, 0u, 0u, 0u};
-      if (row_ok) qraw[ks] = *reinterpret_cast<const u32x4*>(qp + ks * 16);
+    for (int j = 0; j < LPR; ++j) {
+      load_lds16(g_zero16, lds_addr(dst + j * 512));
+      load_lds16(g_zero16, lds_addr(dst + TILE_ELEMS + j * 512));
     }
+  };
+  auto clamp_page = [&](int p) { return min(max(p, 0), a.num_pages - 1); };
+
+  // ---- prologue, part 2: the first NS-1 tiles -----------------------------
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k) {
+    if (k < ntiles) issue_tile(start + k * kTile, clamp_page(pg0[k]), stage_buf[k]);
+    else issue_dummy(stage_buf[k]);
   }
-  int page_ids = 0;                              // lane i: this wavefront's page of tile i
-  if (lane < ntiles) page_ids = trow[page_index(lane)];
 
   // ---- running softmax state (per lane = per query row, this token half) --
   // m_run is a lazily raised reference maximum (log2 units): it only moves
@@ -281,36 +323,41 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   const int tr_dofs = 16 * ((lane >> 4) & 1) + 4 * (trk & 3);   // + db*32
   const int tr_tofs = 4 * half + (trk >> 2);                      // + th*32 + 16*k2 (+8)
 
+  // Raw scores S^T of one tile for this wavefront: this lane's query row
+  // against 16 of the 32 tokens of its half (A = K rows from LDS, B = Q).
+  auto qk = [&](const uint16_t* ks) {
+    const int tok = th * 32 + col;
+    bf16x8 kf[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int gk = kk * 2 + half;
+      kf[kk] = *reinterpret_cast<const bf16x8*>(ks + tok * D + ((gk ^ (tok & (KG - 1))) * 8));
+    }
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], __builtin_bit_cast(bf16x8, qraw[kk]), acc, 0, 0, 0);
+    return acc;
+  };
+
+  // Software pipeline: iteration t holds the raw scores of tile t on entry,
+  // takes its softmax statistics, waits for tile t+1, and then computes the
+  // scores of tile t+1 (matrix cores) together with P of tile t (vector
+  // ALU) before P.V of tile t.  The stage of tile t-1 is free once tile t+1
+  // has landed, and tile t-1+NS goes there, so NS-2 tiles stay in flight.
+  wait_vmcnt<(NS - 2) * LPT>();                                  // tile 0 has landed
+  lds_barrier();
+  f32x16 sacc = f32x16{};
+  if (wave_rows) sacc = qk(stage_buf[0]);
+
   for (int t0 = 0; t0 < ntiles; t0 += NS) {
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       const int t = t0 + k;
       if (t >= ntiles) break;                                      // uniform
       const int ts = start + t * kTile;
-      uint16_t* const sbuf = stage_buf[k];
-      wait_tiles_outstanding<LPT>(min(NS - 2, ntiles - 1 - t));   // tile t has landed
-      lds_barrier();                                               // ... for every wavefront
-      if (t + NS - 1 < ntiles)
-        issue_tile(ts + (NS - 1) * kTile, clamp_page(__builtin_amdgcn_readlane(page_ids, t + NS - 1)),
-                   stage_buf[(k + NS - 1) % NS]);
-
+      float m_use = 0.f;
       if (wave_rows) {
-        const uint16_t* ks = sbuf;
-        const uint16_t* vs = sbuf + TILE_ELEMS;
-        f32x16 sacc = f32x16{};
-        {
-          const int tok = th * 32 + col;
-          bf16x8 kf[KS];
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk) {
-            const int gk = kk * 2 + half;
-            kf[kk] = *reinterpret_cast<const bf16x8*>(ks + tok * D + ((gk ^ (tok & (KG - 1))) * 8));
-          }
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk)
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], __builtin_bit_cast(bf16x8, qraw[kk]),
-                                                           sacc, 0, 0, 0);
-        }
         // mask what this row may not see (raw scores; the scale is positive)
         const int tok0 = ts + th * 32;
         if (tok0 + 31 > row_limit) {
@@ -325,7 +372,30 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
         for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[v]);
         tmax = xor32_max(tmax) * c;
         const float m_new = tmax > m_run + 8.0f ? tmax : m_run;
-        const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+        m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+        if (__any(m_new != m_run)) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        }
+        m_run = m_new;
+      }
+      // Tile t+1 (a zero tile after the last one) has landed for this
+      // wavefront; waiting also on the last step keeps the wait count the
+      // same on every path, which the compiler's own wait insertion needs.
+      wait_vmcnt<(NS - 3) * LPT>();
+      if (t + 1 < ntiles) {                                        // uniform
+        lds_barrier();                                             // ... for every wavefront
+        if (t - 1 + NS < ntiles)
+          issue_tile(ts + (NS - 1) * kTile, clamp_page(__builtin_amdgcn_readlane(page_ids, t - 1 + NS)),
+                     stage_buf[(k + NS - 1) % NS]);
+        else
+          issue_dummy(stage_buf[(k + NS - 1) % NS]);
+      }
+      if (wave_rows) {
+        // scores of tile t+1 (after the last tile: stale LDS, never used)
+        const f32x16 snext = qk(stage_buf[(k + 1) % NS]);
         float lsum = 0.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -333,15 +403,8 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
           sacc[v] = pv;
           lsum += pv;
         }
-        if (__any(m_new != m_run)) {
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-          l_run *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-        }
         l_run += lsum;
-        m_run = m_new;
-
+        const uint16_t* vs = stage_buf[k] + TILE_ELEMS;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
           bf16x8 pb;
@@ -362,12 +425,14 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
           for (int db = 0; db < DB; ++db)
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb, oacc[db], 0, 0, 0);
         }
+        sacc = snext;
       }
     }
   }
 
   // ---- merge the two token halves of each row group through LDS ----------
   l_run = xor32_sum(l_run);
+  wait_vmcnt<0>();                                 // trailing zero-tile loads have landed
   lds_barrier();                                   // every wavefront is done with the ring
   // rows padded by 4 floats: lane col writes row col, and the padding puts
   // consecutive rows on different LDS banks
@@ -420,16 +485,20 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
 // Merge the split partials of every output row:
 //   out = sum_s w_s l_s Ohat_s / sum_s w_s l_s,  w_s = 2^(m_s - M),  M = max_s m_s,
 // with Ohat_s = O_s / l_s (bf16).  One wavefront per output row: lane s % 64
-// reads split s's (m, l); D/8 lanes cover the row (8 values, 16 bytes each)
-// and the 64/(D/8) lane groups take interleaved splits in increasing order,
-// four loads in flight per lane; the group sums are added in group order.
-// Splits a row cannot see contribute exact zeros, so the result does not
-// depend on how many splits the call had.
+// holds split s's (m, l); D/8 lanes cover the row (8 values, 16 bytes each)
+// and the 64/(D/8) lane groups take interleaved splits in increasing order;
+// the group sums are added in group order.  The first batch of partial rows
+// is loaded together with the (m, l) pairs, since Ohat_s does not depend on
+// M, so a row with up to 8 splits per lane group costs one memory round
+// trip.  Splits a row cannot see contribute exact zeros, so the result does
+// not depend on how many splits the call had.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
   constexpr int TPR = D / 8;      // lanes per row slice
   constexpr int SG = 64 / TPR;    // split groups per wavefront
-  constexpr int U = 4;            // splits in flight per lane group
+  constexpr int U = 8;            // splits per lane group per batch
+  constexpr int BATCH = U * SG;   // splits per batch (divides 64)
+  static_assert(64 % BATCH == 0, "a batch stays inside one group of 64 splits");
   const int lane = threadIdx.x & 63;
   const int orow = blockIdx.x * 4 + (threadIdx.x >> 6);   // (b, i, h) flattened
   if (orow >= a.B * a.K * a.Hq) return;                    // uniform per wavefront
@@ -443,50 +512,66 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
   const int r = i * a.G + (h - g * a.G);
   const int chunk = r / kMaxRowsPerCta;
   const int rl = r - chunk * kMaxRowsPerCta;
-  const int L = clamp_len(a.seq_lens[b], a.max_ctx);
-  const int ns = (L + a.K + a.split - 1) / a.split;
   const int Hkv = a.Hq / a.G;
   const size_t prow0 = ((size_t(b) * Hkv + g) * a.nchunks + chunk) * a.nsplit * a.rpc + rl;
   const float* ml = a.part_ml + prow0 * 2;
   const uint16_t* po = a.part_o + prow0 * D + d0;
   const size_t ml_stride = size_t(a.rpc) * 2, o_stride = size_t(a.rpc) * D;
 
-  float M = -__builtin_inff();
-  for (int s0 = 0; s0 < ns; s0 += 64)
-    if (s0 + lane < ns) M = fmaxf(M, ml[(s0 + lane) * ml_stride]);
+  // Loads are bounded by the call's split count only, so they need not wait
+  // for the sequence length; slots of splits >= ns hold nothing of this call
+  // and are discarded by selects (never multiplied: they may hold any bits).
+  auto load_ml = [&](int s) {
+    f32x2 e = {-__builtin_inff(), 0.f};
+    if (s < a.nsplit) e = *reinterpret_cast<const f32x2*>(ml + s * ml_stride);
+    return e;
+  };
+  auto load_batch = [&](int j0, u32x4* raw) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * SG + sg;
+      raw[u] = u32x4{0u, 0u, 0u, 0u};
+      if (j < a.nsplit) raw[u] = *reinterpret_cast<const u32x4*>(po + j * o_stride);
+    }
+  };
+
+  // one round trip: (m, l) of splits 0..63 and the first batch of partial rows
+  f32x2 e = load_ml(lane);
+  u32x4 raw[U];
+  load_batch(0, raw);
+  const int L = clamp_len(a.seq_lens[b], a.max_ctx);
+  const int ns = (L + a.K + a.split - 1) / a.split;
+  float M = lane < ns ? e[0] : -__builtin_inff();
+  for (int s0 = 64; s0 < ns; s0 += 64) {
+    const float m = load_ml(s0 + lane)[0];
+    if (s0 + lane < ns) M = fmaxf(M, m);
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   const float M_use = (M == -__builtin_inff()) ? 0.f : M;
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 64) {
-    float wl = 0.f;                                   // w_s * l_s of split s0 + lane
-    if (s0 + lane < ns) {
-      const float* e = ml + (s0 + lane) * ml_stride;
-      wl = __builtin_amdgcn_exp2f(e[0] - M_use) * e[1];
-    }
-    const int cnt = min(64, ns - s0);
-    for (int jj = 0; jj < cnt; jj += U * SG) {
-      u32x4 raw[U];
-      float w[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = jj + u * SG + sg;               // this lane group's split
-        w[u] = __shfl(wl, j & 63);
-        raw[u] = u32x4{0u, 0u, 0u, 0u};
-        if (j < cnt) raw[u] = *reinterpret_cast<const u32x4*>(po + (s0 + j) * o_stride);
+  float wl = lane < ns ? __builtin_amdgcn_exp2f(e[0] - M_use) * e[1] : 0.f;   // w_s l_s, s = lane
+  for (int j0 = 0; j0 < ns; j0 += BATCH) {
+    if (j0 > 0) {
+      if ((j0 & 63) == 0) {                       // next group of 64 splits
+        e = load_ml(j0 + lane);
+        wl = j0 + lane < ns ? __builtin_amdgcn_exp2f(e[0] - M_use) * e[1] : 0.f;
       }
+      load_batch(j0, raw);
+    }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (jj + u * SG + sg < cnt) {
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * SG + sg;
+      const float w = __shfl(wl, j & 63);
+      if (j < ns) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[2 * q] += w[u] * bf16_lo(raw[u][q]);
-            acc[2 * q + 1] += w[u] * bf16_hi(raw[u][q]);
-          }
-          lsum += w[u];
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += w * bf16_lo(raw[u][q]);
+          acc[2 * q + 1] += w * bf16_hi(raw[u][q]);
         }
+        lsum += w;
       }
     }
   }
