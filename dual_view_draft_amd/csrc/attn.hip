@@ -133,6 +133,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // later LDS read touches another ring stage, it would wait for every load in
 // flight before that read, draining the ring.  The ring's own vmcnt waits
 // and barriers order each read after the loads that fill its stage.
+// m0 is a register the compiler reserves; nothing else in these kernels takes
+// an m0 operand (the LDS reads, barriers and lane reads here do not), so the
+// clobber is safe and the warning about it is silenced for this function.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
@@ -142,6 +147,7 @@ __device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
       : "s"(lds), "v"(src)
       : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -465,21 +471,45 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   const size_t part = ((size_t(b) * a.Hkv + g) * a.nchunks + chunk) * a.nsplit + s;
   const size_t prow = part * a.rpc + rg * kRowsPerWave + col;
   uint16_t* po = a.part_o + prow * D;
+  // All of the other half's values first (one LDS round trip), then the
+  // merged, normalised bf16 values: lane half h holds d = 32 db + 8 j + 4 h
+  // + 0..3.  Pairs of lanes l, l^32 then trade 8-byte pieces so that every
+  // lane writes 16 consecutive bytes (8 values).
+  f32x4 ob[DB * 4];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 ob = *reinterpret_cast<const f32x4*>(xo + col * XS + db * 32 + 8 * j + 4 * half);
-      float o[4];
+    for (int j = 0; j < 4; ++j)
+      ob[db * 4 + j] = *reinterpret_cast<const f32x4*>(xo + col * XS + db * 32 + 8 * j + 4 * half);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = (wa * oacc[db][4 * j + i] + wb * ob[i]) * inv;
-      const u32x2 w2 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-      *reinterpret_cast<u32x2*>(po + db * 32 + 8 * j + 4 * half) = w2;
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      uint32_t w[2][2];                            // [j - 2 jp][pair]
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * jp + jj;
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (wa * oacc[db][4 * j + i] + wb * ob[db * 4 + j][i]) * inv;
+        w[jj][0] = pack_bf16x2(o[0], o[1]);
+        w[jj][1] = pack_bf16x2(o[2], o[3]);
+      }
+      // half 0 keeps j = 2jp (d 0..3 of the 16) and sends j = 2jp+1; half 1
+      // keeps j = 2jp+1 (d 12..15) and sends j = 2jp
+      const bool hi = half != 0;
+      u32x4 out4;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t x = hi ? w[0][q] : w[1][q];
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        const uint32_t other = hi ? r[0] : r[1];          // the partner's sent piece
+        out4[q] = hi ? other : w[0][q];
+        out4[2 + q] = hi ? w[1][q] : other;
+      }
+      *reinterpret_cast<u32x4*>(po + db * 32 + 16 * jp + 8 * half) = out4;
     }
-  if (half == 0) {
-    a.part_ml[prow * 2 + 0] = M;
-    a.part_ml[prow * 2 + 1] = l_tot;
-  }
+  if (half == 0) *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) = f32x2{M, l_tot};
 }
 
 // Merge the split partials of every output row:
