@@ -318,6 +318,53 @@ def make_prompt(seed: int, n: int, vocab: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Named workloads (sizes and seeds)
 # --------------------------------------------------------------------------
+# LM head (final hidden states x vocabulary weights)
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LmHeadCase:
+    hidden: np.ndarray   # [R, hidden] bf16 bits (after the final norm)
+    weight: np.ndarray   # [V, hidden] bf16 bits
+    targets: np.ndarray  # [R] int32 planted token per row, -1 if none
+
+
+def make_lmhead_case(seed: int, R: int, hidden: int, V: int, *, plant: bool = True,
+                     lift: float = 30.0, w_std: float = 0.02, dup_rows: int = 0) -> LmHeadCase:
+    """Hidden states N(0,1) and LM-head weights N(0, w_std) rounded to bf16.
+
+    With ``plant``, row r gets a target token t_r (distinct across rows when
+    V >= R): W[t_r] += lift * h_r / |h_r|^2 before rounding, which raises that
+    logit by about ``lift`` (the background logits have standard deviation
+    w_std * sqrt(hidden), 1.28 at hidden 4096).  ``dup_rows`` copies the
+    weight row of each of the first ``dup_rows`` targets to a random lower
+    vocabulary index, so the maximum is attained twice."""
+    rng = np.random.default_rng(seed)
+    h32 = rng.standard_normal((R, hidden), dtype=np.float32)
+    h_bits = f32_to_bf16_bits(h32)
+    w32 = rng.standard_normal((V, hidden), dtype=np.float32) * np.float32(w_std)
+    targets = np.full(R, -1, dtype=np.int32)
+    if plant:
+        t = rng.choice(V, size=R, replace=V < R).astype(np.int32)
+        hf = bf16_bits_to_f32(h_bits)
+        for r in range(R):
+            w32[t[r]] += np.float32(lift) * hf[r] / np.float32(np.dot(hf[r], hf[r]))
+        targets = t
+    w_bits = f32_to_bf16_bits(w32)
+    taken = set(int(x) for x in targets)
+    for r in range(min(dup_rows, R)):
+        free = [v for v in range(int(targets[r])) if v not in taken] if targets[r] > 0 else []
+        if free:
+            lower = int(free[int(rng.integers(0, len(free)))])
+            w_bits[lower] = w_bits[targets[r]]
+            taken.add(lower)
+            targets[r] = lower
+    return LmHeadCase(h_bits, w_bits, targets)
+
+
+__all__ += ["LmHeadCase", "make_lmhead_case"]
+
+
+# --------------------------------------------------------------------------
 
 WORKLOADS = {
     # tiny CPU-checkable case
