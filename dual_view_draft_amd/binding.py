@@ -54,6 +54,12 @@ EXPORTS = {
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "orthrus_accept": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 3 +
                        [ctypes.c_void_p] * 4 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "orthrus_lmhead_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 3),
+    "orthrus_lmhead_argmax": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 3 +
+                              [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                               ctypes.c_void_p]),
+    "orthrus_lmhead_accept": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 +
+                              [ctypes.c_void_p] * 4 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "orthrus_commit_kv": (ctypes.c_int, [ctypes.POINTER(orthrus_kv), ctypes.c_int, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
@@ -230,6 +236,54 @@ def orthrus_accept(logits_a: torch.Tensor, draft: torch.Tensor, ar_tokens, n_acc
                                        _ptr(n_acc), _ptr(n_emit), _ptr(next_anchor),
                                        _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "orthrus_accept")
+
+
+def orthrus_lmhead_workspace_bytes(rows: int, hidden: int, vocab: int) -> int:
+    return load_library().orthrus_lmhead_workspace_bytes(rows, hidden, vocab)
+
+
+def lmhead_workspace(rows: int, hidden: int, vocab: int, device) -> torch.Tensor:
+    n = orthrus_lmhead_workspace_bytes(rows, hidden, vocab)
+    if n == 0:
+        raise ValueError("unsupported LM-head shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def orthrus_lmhead_argmax(hidden_states: torch.Tensor, weight: torch.Tensor, out: torch.Tensor, *,
+                          logits=None, workspace=None, stream=None):
+    """out[r] = greedy token of hidden_states[r] (bf16 [..., hidden]) under the LM head
+    weight (bf16 [V, hidden]); logits (fp32 [rows, V]) optionally receives the logits."""
+    if hidden_states.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise ValueError("hidden_states and weight must be bfloat16")
+    if out.dtype != torch.int32 or (logits is not None and logits.dtype != torch.float32):
+        raise ValueError("out must be int32 and logits float32")
+    V, Hd = weight.shape
+    rows = hidden_states.numel() // Hd
+    if workspace is None:
+        workspace = lmhead_workspace(rows, Hd, V, hidden_states.device)
+    rc = load_library().orthrus_lmhead_argmax(_ptr(hidden_states), _ptr(weight), rows, Hd, V, _ptr(out),
+                                              _ptr(logits) if logits is not None else None,
+                                              _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "orthrus_lmhead_argmax")
+    return out
+
+
+def orthrus_lmhead_accept(hidden_states: torch.Tensor, weight: torch.Tensor, draft: torch.Tensor,
+                          ar_tokens, n_acc, n_emit, next_anchor, *, workspace=None, stream=None):
+    """Consensus from the verify pass's final hidden states [B, K, hidden] (bf16)."""
+    if hidden_states.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise ValueError("hidden_states and weight must be bfloat16")
+    for t in (draft, ar_tokens, n_acc, n_emit, next_anchor):
+        if t.dtype != torch.int32:
+            raise ValueError("token and count tensors must be int32")
+    B, K, Hd = hidden_states.shape
+    V = weight.shape[0]
+    if workspace is None:
+        workspace = lmhead_workspace(B * K, Hd, V, hidden_states.device)
+    rc = load_library().orthrus_lmhead_accept(_ptr(hidden_states), _ptr(weight), _ptr(draft), B, K, Hd, V,
+                                              _ptr(ar_tokens), _ptr(n_acc), _ptr(n_emit), _ptr(next_anchor),
+                                              _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "orthrus_lmhead_accept")
 
 
 def orthrus_commit_kv(kv_layer0: PagedKV, k_blk: torch.Tensor, v_blk: torch.Tensor,

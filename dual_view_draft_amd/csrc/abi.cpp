@@ -120,6 +120,55 @@ int orthrus_accept(const float* logits_a, const int32_t* draft, int batch, int b
   }
 }
 
+size_t orthrus_lmhead_workspace_bytes(int rows, int hidden, int vocab) {
+  orthrus::LmHeadPlan plan;
+  if (!orthrus::plan_lmhead(rows, hidden, vocab, &plan, nullptr)) return 0;
+  return plan.ws_bytes;
+}
+
+int orthrus_lmhead_argmax(const void* hidden_states, const void* weight, int rows, int hidden, int vocab,
+                          int32_t* out, float* logits, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  try {
+    orthrus::LmHeadPlan plan;
+    std::string err;
+    const int rc = orthrus::check_lmhead(hidden_states, weight, rows, hidden, vocab, out, workspace,
+                                         workspace_bytes, &plan, &err);
+    if (rc != ORTHRUS_OK) return fail(rc, err);
+    if (rows == 0) return ORTHRUS_OK;
+    hipStream_t s = as_stream(stream);
+    hipError_t e = orthrus::launch_lmhead(plan, hidden_states, weight, logits, workspace, s);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(orthrus::launch_argmax_keys(static_cast<const unsigned long long*>(workspace), rows,
+                                                  plan.nwg, out, s));
+  } catch (...) {
+    return fail(ORTHRUS_ERR_HIP, "internal error");
+  }
+}
+
+int orthrus_lmhead_accept(const void* hidden_states, const void* weight, const int32_t* draft, int batch,
+                          int block_k, int hidden, int vocab, int32_t* ar_tokens, int32_t* n_acc,
+                          int32_t* n_emit, int32_t* next_anchor, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  try {
+    orthrus::LmHeadPlan plan;
+    std::string err;
+    const int rc = orthrus::check_lmhead_accept(hidden_states, weight, draft, batch, block_k, hidden, vocab,
+                                                ar_tokens, n_acc, n_emit, next_anchor, workspace,
+                                                workspace_bytes, &plan, &err);
+    if (rc != ORTHRUS_OK) return fail(rc, err);
+    if (batch == 0) return ORTHRUS_OK;
+    hipStream_t s = as_stream(stream);
+    hipError_t e = orthrus::launch_lmhead(plan, hidden_states, weight, nullptr, workspace, s);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(orthrus::launch_accept_keys(static_cast<const unsigned long long*>(workspace), plan.nwg,
+                                                  draft, batch, block_k, ar_tokens, n_acc, n_emit,
+                                                  next_anchor, s));
+  } catch (...) {
+    return fail(ORTHRUS_ERR_HIP, "internal error");
+  }
+}
+
 int orthrus_commit_kv(const orthrus_kv* kv, int num_layers, int64_t pool_layer_stride,
                       const void* k_blk, const void* v_blk, int64_t blk_layer_stride,
                       const int32_t* n_emit, int batch, int block_k, int32_t* seq_lens_out,

@@ -154,6 +154,53 @@ int check_accept(const float* logits_a, const int32_t* draft, int B, int K, int 
   return ORTHRUS_OK;
 }
 
+bool plan_lmhead(int rows, int hidden, int V, LmHeadPlan* p, std::string* why) {
+  auto no = [&](const char* m) { if (why) *why = m; return false; };
+  if (rows < 0) return no("rows must be >= 0");
+  if (V < 1) return no("vocab must be >= 1");
+  if (hidden < kLmKTile || hidden % kLmKTile || hidden > (1 << 20))
+    return no("hidden must be a multiple of 64 in [64, 2^20]");
+  if (int64_t(rows) * V > (int64_t(1) << 40)) return no("rows * vocab too large");
+  p->rows = rows; p->hidden = hidden; p->V = V;
+  p->nwg = V < kLmWorkgroups ? V : kLmWorkgroups;
+  p->nrc = int(ceil_div(rows, kLmRowChunk));
+  p->ws_bytes = size_t(round_up(int64_t(rows > 0 ? rows : 1) * p->nwg * 8, 256));
+  return true;
+}
+
+int check_lmhead(const void* hidden_states, const void* weight, int rows, int hidden, int V,
+                 const int32_t* out, const void* ws, size_t ws_bytes, LmHeadPlan* plan, std::string* err) {
+  std::string why;
+  if (!plan_lmhead(rows, hidden, V, plan, &why)) {
+    if (err) *err = why;
+    return (rows < 0 || V < 1) ? ORTHRUS_ERR_INVALID_ARG : ORTHRUS_ERR_UNSUPPORTED_SHAPE;
+  }
+  if (rows > 65535 * kLmRowChunk) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "too many rows per call");
+  if (rows == 0) return ORTHRUS_OK;
+  if (!hidden_states || !weight || !out) return fail(err, ORTHRUS_ERR_INVALID_ARG, "null hidden/weight/out");
+  if (!aligned16(hidden_states) || !aligned16(weight))
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "hidden/weight must be 16-byte aligned");
+  if (!ws || !aligned16(ws)) return fail(err, ORTHRUS_ERR_INVALID_ARG, "workspace null or misaligned");
+  if (ws_bytes < plan->ws_bytes)
+    return fail(err, ORTHRUS_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than orthrus_lmhead_workspace_bytes()");
+  return ORTHRUS_OK;
+}
+
+int check_lmhead_accept(const void* hidden_states, const void* weight, const int32_t* draft, int B, int K,
+                        int hidden, int V, const int32_t* a, const int32_t* n_acc, const int32_t* n_emit,
+                        const int32_t* next_anchor, const void* ws, size_t ws_bytes, LmHeadPlan* plan,
+                        std::string* err) {
+  if (B < 0) return fail(err, ORTHRUS_ERR_INVALID_ARG, "batch must be >= 0");
+  if (K < 1 || K > ORTHRUS_MAX_BLOCK) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "block_k must be in [1, 64]");
+  if (int64_t(B) * K > (int64_t(1) << 30)) return fail(err, ORTHRUS_ERR_INVALID_ARG, "batch * block_k too large");
+  int rc = check_lmhead(hidden_states, weight, B * K, hidden, V, a, ws, ws_bytes, plan, err);
+  if (rc) return rc;
+  if (B == 0) return ORTHRUS_OK;
+  if (!draft || !n_acc || !n_emit || !next_anchor)
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "null draft/n_acc/n_emit/next_anchor");
+  return ORTHRUS_OK;
+}
+
 int check_commit(const orthrus_kv* kv, int layers, int64_t pool_layer_stride, const void* k_blk,
                  const void* v_blk, int64_t blk_layer_stride, const int32_t* n_emit, int B, int K,
                  const int32_t* seq_lens_out, std::string* err) {

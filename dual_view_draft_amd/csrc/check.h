@@ -34,6 +34,19 @@ struct ArgmaxPlan {
   size_t ws_bytes = 0;
 };
 
+// LM head + argmax: one workgroup per contiguous vocabulary range (one per
+// CU of an MI355X), query rows in chunks of 32, hidden in tiles of 64.
+constexpr int kLmWorkgroups = 256;
+constexpr int kLmRowChunk = 32;
+constexpr int kLmKTile = 64;
+
+struct LmHeadPlan {
+  int rows = 0, hidden = 0, V = 0;
+  int nwg = 0;           // vocabulary ranges = argmax key chunks per row
+  int nrc = 0;           // row chunks of kLmRowChunk rows
+  size_t ws_bytes = 0;   // keys [rows][nwg] (8 bytes each)
+};
+
 int attn_split_tokens(int B, int Hkv, int max_ctx);
 
 // Shape-only planning (no pointers); false if the shape is unsupported.
@@ -55,6 +68,16 @@ int check_accept(const float* logits_a, const int32_t* draft, int B, int K, int 
                  const int32_t* a, const int32_t* n_acc, const int32_t* n_emit,
                  const int32_t* next_anchor, const void* ws, size_t ws_bytes, ArgmaxPlan* plan,
                  std::string* err);
+
+bool plan_lmhead(int rows, int hidden, int V, LmHeadPlan* plan, std::string* why);
+
+int check_lmhead(const void* hidden_states, const void* weight, int rows, int hidden, int V,
+                 const int32_t* out, const void* ws, size_t ws_bytes, LmHeadPlan* plan, std::string* err);
+
+int check_lmhead_accept(const void* hidden_states, const void* weight, const int32_t* draft, int B, int K,
+                        int hidden, int V, const int32_t* a, const int32_t* n_acc, const int32_t* n_emit,
+                        const int32_t* next_anchor, const void* ws, size_t ws_bytes, LmHeadPlan* plan,
+                        std::string* err);
 
 int check_commit(const orthrus_kv* kv, int layers, int64_t pool_layer_stride, const void* k_blk,
                  const void* v_blk, int64_t blk_layer_stride, const int32_t* n_emit, int B, int K,

@@ -21,6 +21,7 @@
 #include <cstdint>
 
 #include "check.h"
+#include "keys.h"
 #include "launch.h"
 
 namespace orthrus {
@@ -50,22 +51,6 @@ struct AcceptArgs {
   int B, K, nchunks;
 };
 
-// Monotone map float -> uint32 (-0.0 and +0.0 map to the same key).
-__device__ __forceinline__ uint32_t ordered_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ unsigned long long make_key(float x, int idx) {
-  return (static_cast<unsigned long long>(ordered_bits(x)) << 32) |
-         static_cast<unsigned long long>(~static_cast<uint32_t>(idx));
-}
-
-__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
-  return a > b ? a : b;
-}
-
 __device__ __forceinline__ unsigned long long wave_max(unsigned long long k) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -74,10 +59,6 @@ __device__ __forceinline__ unsigned long long wave_max(unsigned long long k) {
     k = umax64(k, (static_cast<unsigned long long>(hi) << 32) | lo);
   }
   return k;
-}
-
-__device__ __forceinline__ int32_t key_index(unsigned long long k) {
-  return static_cast<int32_t>(~static_cast<uint32_t>(k));
 }
 
 __global__ __launch_bounds__(256) void argmax_partial_kernel(PartialArgs a) {
@@ -180,12 +161,24 @@ hipError_t launch_partial(const ArgmaxPlan& p, const float* logits, void* ws, hi
 
 }  // namespace
 
+hipError_t launch_argmax_keys(const unsigned long long* keys, int rows, int nchunks, int32_t* out,
+                              hipStream_t stream) {
+  FinalArgs f{keys, out, rows, nchunks};
+  return launch_kernel(&argmax_final_kernel, dim3((rows + 3) / 4), dim3(256), stream, f);
+}
+
+hipError_t launch_accept_keys(const unsigned long long* keys, int nchunks, const int32_t* draft, int B,
+                              int K, int32_t* a, int32_t* n_acc, int32_t* n_emit, int32_t* next_anchor,
+                              hipStream_t stream) {
+  AcceptArgs x{keys, draft, a, n_acc, n_emit, next_anchor, B, K, nchunks};
+  return launch_kernel(&accept_kernel, dim3(B), dim3(256), stream, x);
+}
+
 hipError_t launch_argmax(const ArgmaxPlan& p, const float* logits, int32_t* out, void* ws,
                          hipStream_t stream) {
   hipError_t e = launch_partial(p, logits, ws, stream);
   if (e != hipSuccess) return e;
-  FinalArgs f{static_cast<const unsigned long long*>(ws), out, p.rows, p.nchunks};
-  return launch_kernel(&argmax_final_kernel, dim3((p.rows + 3) / 4), dim3(256), stream, f);
+  return launch_argmax_keys(static_cast<const unsigned long long*>(ws), p.rows, p.nchunks, out, stream);
 }
 
 hipError_t launch_accept(const ArgmaxPlan& p, const float* logits_a, const int32_t* draft, int B,
@@ -193,9 +186,8 @@ hipError_t launch_accept(const ArgmaxPlan& p, const float* logits_a, const int32
                          void* ws, hipStream_t stream) {
   hipError_t e = launch_partial(p, logits_a, ws, stream);
   if (e != hipSuccess) return e;
-  AcceptArgs x{static_cast<const unsigned long long*>(ws), draft, a, n_acc, n_emit, next_anchor,
-               B, K, p.nchunks};
-  return launch_kernel(&accept_kernel, dim3(B), dim3(256), stream, x);
+  return launch_accept_keys(static_cast<const unsigned long long*>(ws), p.nchunks, draft, B, K, a, n_acc,
+                            n_emit, next_anchor, stream);
 }
 
 }  // namespace orthrus

@@ -29,6 +29,20 @@ hipError_t launch_accept(const ArgmaxPlan& plan, const float* logits_a, const in
                          int B, int K, int32_t* a, int32_t* n_acc, int32_t* n_emit,
                          int32_t* next_anchor, void* ws, hipStream_t stream);
 
+// Row maxima of per-chunk argmax keys [rows][nchunks] (keys.h).
+hipError_t launch_argmax_keys(const unsigned long long* keys, int rows, int nchunks, int32_t* out,
+                              hipStream_t stream);
+
+// Acceptance from per-chunk keys of the AR view's rows [B*K][nchunks].
+hipError_t launch_accept_keys(const unsigned long long* keys, int nchunks, const int32_t* draft, int B,
+                              int K, int32_t* a, int32_t* n_acc, int32_t* n_emit, int32_t* next_anchor,
+                              hipStream_t stream);
+
+// LM head + per-workgroup argmax keys [rows][plan.nwg] into ws (optionally
+// also the fp32 logits [rows][vocab]).
+hipError_t launch_lmhead(const LmHeadPlan& plan, const void* hidden, const void* weight, float* logits,
+                         void* ws, hipStream_t stream);
+
 hipError_t launch_commit(const orthrus_kv& kv, int layers, int64_t pool_layer_stride,
                          const void* k_blk, const void* v_blk, int64_t blk_layer_stride,
                          const int32_t* n_emit, int B, int K, int32_t* seq_lens_out,

@@ -1,0 +1,190 @@
+// LM head and vocabulary argmax in one pass over the weights, without
+// materialising the logits.
+//
+// Both Orthrus views end in the frozen model's shared LM head; the draft
+// tokens and the AR view's greedy tokens are the argmax of its logits for
+// every block row (gist.science technical summary of "Orthrus:
+// Memory-Efficient Parallel Token Generation via Dual-View Diffusion",
+// section 2.3 steps 1 and 3; Hacker News thread "Orthrus-Qwen3: up to
+// 7.8x tokens/forward ...", post #26: the diffusion module shares the LM
+// head).  For a few rows (B*K = 32 at B = 1) the product is a skinny matrix
+// product bound by reading W [V, hidden] once: 1.24 GB at V = 151936,
+// hidden = 4096, against 19 MB of fp32 logits that need not exist at all.
+//
+// Work decomposition: one workgroup (8 wavefronts) per contiguous vocabulary
+// range [v0, v1) of about V/256 entries, for 32 query rows (grid.y walks row
+// chunks).  The range is cut into blocks of 256 vocabulary rows; wavefront w
+// owns block rows 32w .. 32w+31.  Tiles of 64 hidden elements of the block's
+// weight rows (32 KiB) and of the query rows (4 KiB) stream HBM -> LDS through
+// a 4-stage ring, three tiles in flight, with the same direct-to-LDS loads,
+// fixed waits and zero tiles past the end as the attention kernel.  Per tile
+// a wavefront does 4 MFMA 32x32x16 bf16 steps of
+//     L^T[vocab][row] += W[vocab][k] . h[row][k]
+// (A = weight rows from LDS, B = query rows from LDS), and at the end of a
+// block turns its 32 x 32 fp32 logits into (value, index) keys (keys.h),
+// keeping the best per row in registers.  The workgroup writes one key per
+// row; the final argmax or acceptance kernel reduces the 256 keys of a row.
+// Rows past the last one and vocabulary rows past the range are loaded as
+// zeros and never become keys.  Every logit is one wavefront's sum over the
+// hidden dimension in a fixed order, so the keys, and the tokens, do not
+// depend on the launch shape or on how the maxima are combined.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "check.h"
+#include "keys.h"
+#include "launch.h"
+#include "lds_ring.h"
+
+namespace orthrus {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 16 zero bytes: the source of rows past the end.
+__device__ __attribute__((aligned(16))) uint16_t g_lm_zero16[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+struct LmArgs {
+  const uint16_t* h;         // [rows][hidden] bf16 (final norm applied)
+  const uint16_t* w;         // [V][hidden] bf16
+  float* logits;             // [rows][V] fp32, or null (not written)
+  unsigned long long* keys;  // [rows][nwg]
+  int rows, hidden, V, nwg;
+};
+
+constexpr int VB = 256;               // vocabulary rows per block (8 wavefronts x 32)
+constexpr int KT = kLmKTile;          // hidden elements per tile
+constexpr int RC = kLmRowChunk;       // query rows per workgroup
+constexpr int NS = 4;                 // ring stages
+constexpr int W_ELEMS = VB * KT;      // 32 KiB of weights per tile
+constexpr int H_ELEMS = RC * KT;      // 4 KiB of query rows per tile
+constexpr int STAGE = W_ELEMS + H_ELEMS;
+constexpr int LPT = 5;                // loads per wavefront per tile (4 weight + 1 query/sink)
+static_assert(KT == 64, "8 granules of 16 bytes per tile row");
+
+// Granule c (16 bytes) of tile row r sits at c ^ ((r >> 1) & 7): the 32
+// rows one MFMA operand read touches fall on distinct LDS banks.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+__global__ __launch_bounds__(512, 1) void lmhead_kernel(LmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t ring[NS * STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t sink[512];   // target of the spare loads
+  const int wg = blockIdx.x;
+  const int row0 = blockIdx.y * RC;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int v0 = int((int64_t(a.V) * wg) / a.nwg);
+  const int v1 = int((int64_t(a.V) * (wg + 1)) / a.nwg);
+  const int nkt = a.hidden / KT;
+  const int ntiles = ((v1 - v0 + VB - 1) / VB) * nkt;
+
+  // Loads of tile t into stage st.  Weight rows: instruction i of wavefront
+  // w covers block rows 32w + 8i .. +7, lane l row 32w + 8i + l/8, LDS granule
+  // l%8.  Query rows: wavefronts 0..3, rows 8w + l/8; the others load zeros
+  // into a sink.  Every wavefront issues LPT loads per tile (zeros for rows
+  // outside the range and for tiles past the end), so the waits are fixed
+  // counts.
+  const int lr = lane >> 3, lp = lane & 7;
+  auto issue_tile = [&](int t, uint16_t* st) {
+    if (t >= ntiles) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_lds16(g_lm_zero16, lds_addr(st + (wave * 32 + i * 8) * KT));
+      load_lds16(g_lm_zero16, lds_addr(wave < 4 ? st + W_ELEMS + wave * 8 * KT : sink));
+      return;
+    }
+    const int blk = t / nkt;
+    const int kt = t - blk * nkt;
+    const int vbase = v0 + blk * VB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wave * 32 + i * 8 + lr;
+      const int v = vbase + r;
+      const int c = lp ^ swz(r);
+      const void* src = v < v1 ? static_cast<const void*>(a.w + size_t(v) * a.hidden + kt * KT + c * 8)
+                               : static_cast<const void*>(g_lm_zero16);
+      load_lds16(src, lds_addr(st + (wave * 32 + i * 8) * KT));
+    }
+    if (wave < 4) {
+      const int r = wave * 8 + lr;
+      const int hr = row0 + r;
+      const int c = lp ^ swz(r);
+      const void* src = hr < a.rows ? static_cast<const void*>(a.h + size_t(hr) * a.hidden + kt * KT + c * 8)
+                                    : static_cast<const void*>(g_lm_zero16);
+      load_lds16(src, lds_addr(st + W_ELEMS + wave * 8 * KT));
+    } else {
+      load_lds16(g_lm_zero16, lds_addr(sink));
+    }
+  };
+
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k) issue_tile(k, ring + k * STAGE);
+
+  const int ra = wave * 32 + col;        // weight row of this lane's A operand
+  f32x16 acc = f32x16{};
+  unsigned long long best = 0ull;        // best key of row col over this lane's vocabulary
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmcnt<(NS - 2) * LPT>();        // tile t has landed for this wavefront
+    lds_barrier();                       // ... for every wavefront; stage of t-1 is free
+    const int tn = t + NS - 1;
+    issue_tile(tn, ring + (tn % NS) * STAGE);
+    const uint16_t* wt = ring + (t % NS) * STAGE;
+    const uint16_t* ht = wt + W_ELEMS;
+#pragma unroll
+    for (int ks = 0; ks < KT / 16; ++ks) {
+      const int g = ks * 2 + half;
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(wt + ra * KT + ((g ^ swz(ra)) * 8));
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(ht + col * KT + ((g ^ swz(col)) * 8));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+    }
+    const int blk = t / nkt;
+    if (t - blk * nkt == nkt - 1) {      // uniform: the block's logits are complete
+      // lane l, value v: vocabulary row 32w + 8(v/4) + 4 half + v%4 of the block, query row col
+      const int vb = v0 + blk * VB + wave * 32 + 4 * half;
+      const bool row_ok = row0 + col < a.rows;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int vi = vb + 8 * (v >> 2) + (v & 3);
+        if (vi < v1) {
+          best = umax64(best, make_key(acc[v], vi));
+          if (a.logits && row_ok) a.logits[size_t(row0 + col) * a.V + vi] = acc[v];
+        }
+      }
+      acc = f32x16{};
+    }
+  }
+
+  // lanes l and l^32 cover the same query row: combine, then across wavefronts
+  {
+    const auto lo = __builtin_amdgcn_permlane32_swap(uint32_t(best), uint32_t(best), false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap(uint32_t(best >> 32), uint32_t(best >> 32), false, false);
+    const unsigned long long k0 = (static_cast<unsigned long long>(hi[0]) << 32) | lo[0];
+    const unsigned long long k1 = (static_cast<unsigned long long>(hi[1]) << 32) | lo[1];
+    best = umax64(k0, k1);
+  }
+  wait_vmcnt<0>();                        // trailing zero-tile loads have landed
+  lds_barrier();                          // every wavefront is done with the ring
+  unsigned long long* red = reinterpret_cast<unsigned long long*>(ring);   // [8][32]
+  if (half == 0) red[wave * 32 + col] = best;
+  __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): the LDS writes are done
+  lds_barrier();
+  if (wave == 0 && half == 0 && row0 + col < a.rows) {
+    unsigned long long k = red[col];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) k = umax64(k, red[w * 32 + col]);
+    a.keys[size_t(row0 + col) * a.nwg + wg] = k;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lmhead(const LmHeadPlan& p, const void* hidden, const void* weight, float* logits,
+                         void* ws, hipStream_t stream) {
+  LmArgs a{static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(weight), logits,
+           static_cast<unsigned long long*>(ws), p.rows, p.hidden, p.V, p.nwg};
+  return launch_kernel(&lmhead_kernel, dim3(p.nwg, p.nrc), dim3(512), stream, a);
+}
+
+}  // namespace orthrus

@@ -197,6 +197,47 @@ ORTHRUS_API int orthrus_accept(const float* logits_a, const int32_t* draft, int 
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * LM head fused with the vocabulary argmax (the greedy token of every row),
+ * without materialising the logits.  Both views end in the frozen model's
+ * shared LM head (section 2.3 steps 1 and 3; Hacker News thread
+ * "Orthrus-Qwen3: up to 7.8x tokens/forward ...", post #26: the diffusion
+ * module adds only attention projections).
+ *
+ *   logits[r][v] = sum_k hidden_states[r][k] * weight[v][k]
+ *                  (bf16 products, fp32 accumulation over k in a fixed order)
+ *   out[r]       = smallest v with logits[r][v] == max_v logits[r][v]
+ *
+ *  hidden_states : bf16 [rows][hidden], the final hidden states (final norm
+ *                  applied)
+ *  weight        : bf16 [vocab][hidden], the LM-head weight (row v = token v)
+ *  out           : int32 [rows] (written)
+ *  logits        : NULL, or fp32 [rows][vocab] to also receive the logits the
+ *                  argmax was taken over (bit-identical values; for checking
+ *                  and for callers that need them)
+ *  workspace     : >= orthrus_lmhead_workspace_bytes(rows, hidden, vocab)
+ *                  bytes, 16-byte aligned; contents on entry do not matter.
+ * Requirements: hidden a multiple of 64 in [64, 2^20]; 1 <= vocab < 2^31;
+ * 0 <= rows <= 65535 * 32 (0 = no-op).  The weights are read once per 32
+ * rows (rows beyond 32 re-read them).  NaN logits are outside the contract.
+ */
+ORTHRUS_API size_t orthrus_lmhead_workspace_bytes(int rows, int hidden, int vocab);
+
+ORTHRUS_API int orthrus_lmhead_argmax(const void* hidden_states, const void* weight, int rows, int hidden,
+                          int vocab, int32_t* out, float* logits, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * Consensus from the verify pass's final hidden states: as orthrus_accept,
+ * with the AR tokens a[b][i] computed by the fused LM head + argmax of
+ * orthrus_lmhead_argmax from hidden_states [batch][block_k][hidden].
+ * workspace: >= orthrus_lmhead_workspace_bytes(batch * block_k, hidden, vocab).
+ */
+ORTHRUS_API int orthrus_lmhead_accept(const void* hidden_states, const void* weight, const int32_t* draft,
+                          int batch, int block_k, int hidden, int vocab, int32_t* ar_tokens,
+                          int32_t* n_acc, int32_t* n_emit, int32_t* next_anchor, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * Commit (section 2.3 step 3; the single shared cache keeps only what the AR
  * view confirmed): for every layer l, sequence b and row r < n_emit[b], copy
  * the verify pass's k_blk/v_blk row [l][b][r] (all KV heads) bit for bit to

@@ -127,3 +127,21 @@ def test_host_checks_under_sanitizers(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "OK (0 failures)" in r.stdout
+
+
+def test_lmhead_workspace_and_argument_checks(lib):
+    P = ctypes.c_void_p(0x10000)
+    n = lib.orthrus_lmhead_workspace_bytes(32, 4096, 151936)
+    assert n >= 32 * 256 * 8
+    assert lib.orthrus_lmhead_workspace_bytes(32, 100, 151936) == 0      # hidden not a multiple of 64
+    assert lib.orthrus_lmhead_workspace_bytes(32, 4096, 0) == 0
+    assert lib.orthrus_lmhead_workspace_bytes(3, 64, 10) >= 3 * 10 * 8    # one workgroup per token
+    assert lib.orthrus_lmhead_argmax(None, None, 0, 4096, 151936, None, None, None, 0, None) == 0
+    assert lib.orthrus_lmhead_argmax(P, P, 4, 100, 1000, P, None, P, 1 << 20, None) == -2
+    assert lib.orthrus_lmhead_argmax(P, P, 4, 128, 0, P, None, P, 1 << 20, None) == -1
+    assert lib.orthrus_lmhead_argmax(P, P, 4, 128, 1000, P, None, P, 8, None) == -3
+    assert lib.orthrus_lmhead_argmax(ctypes.c_void_p(0x10008), P, 4, 128, 1000, P, None, P, 1 << 20,
+                                     None) == -1                            # misaligned hidden
+    assert lib.orthrus_lmhead_accept(P, P, P, 1, 65, 128, 1000, P, P, P, P, P, 1 << 20, None) == -2
+    assert lib.orthrus_lmhead_accept(None, None, None, 0, 32, 128, 1000, None, None, None, None, None, 0,
+                                     None) == 0

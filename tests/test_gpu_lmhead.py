@@ -1,0 +1,111 @@
+"""GPU parity of the fused LM head + argmax (orthrus_lmhead_argmax,
+orthrus_lmhead_accept) against the oracle.
+
+The tokens are integers decided by floating point: the fused kernel's own
+fp32 logits (written on request by the same launch) must give exactly the
+same argmax, those logits must lie within the fp32 summation bound of the
+fp64 oracle logits, and the chosen token must be an oracle maximum up to that
+bound (exactly the oracle's token where a planted winner leads by far)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import bf16_dev, i32_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    import dual_view_draft_amd as dv
+    dv.load_library()
+    return dv
+
+
+def run(dv, c, with_logits=True):
+    h, w = bf16_dev(c.hidden), bf16_dev(c.weight)
+    R, V = c.hidden.shape[0], c.weight.shape[0]
+    out = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    logits = torch.full((R, V), float("nan"), dtype=torch.float32, device="cuda") if with_logits else None
+    dv.orthrus_lmhead_argmax(h, w, out, logits=logits)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (logits.cpu().numpy() if with_logits else None)
+
+
+def check_against_oracle(c, tok, logits, exact_tokens):
+    from oracle import from_bf16
+    from oracle.lmhead import lm_argmax, lm_logits
+    ref = lm_logits(c.hidden, c.weight)
+    # |fp32 sum - exact| <= hidden * 2^-23 * sum_k |h_k w_k| for every logit
+    bound = c.hidden.shape[1] * 2.0 ** -23 * (np.abs(from_bf16(c.hidden)) @ np.abs(from_bf16(c.weight)).T)
+    # 1. the fused argmax is the argmax of the launch's own fp32 logits, bit for bit
+    own = logits.max(axis=1, keepdims=True)
+    assert np.array_equal(tok, (logits == own).argmax(axis=1).astype(np.int32))
+    # 2. those logits are the oracle's within the summation bound
+    err = np.abs(logits - ref)
+    assert np.all(err <= bound + 1e-30), f"max err {err.max():.3e} vs bound {bound.max():.3e}"
+    # 3. the chosen token is an oracle maximum up to twice the bound
+    rows = np.arange(len(tok))
+    assert np.all(ref[rows, tok] >= ref.max(axis=1) - 2 * bound.max(axis=1))
+    if exact_tokens:
+        assert np.array_equal(tok, lm_argmax(c.hidden, c.weight))
+
+
+@pytest.mark.parametrize("R,Hd,V", [(32, 256, 5000), (7, 128, 777), (1, 64, 1), (40, 128, 3000),
+                                    (32, 4096, 20011), (3, 64, 10), (65, 192, 300)])
+def test_planted_winner(lib, R, Hd, V):
+    from synth import make_lmhead_case
+    c = make_lmhead_case(R * 31 + V, R, Hd, V)
+    tok, logits = run(lib, c)
+    check_against_oracle(c, tok, logits, exact_tokens=True)
+    assert np.array_equal(tok, c.targets)
+
+
+@pytest.mark.parametrize("R,Hd,V", [(32, 4096, 50000), (16, 512, 7777)])
+def test_random_rows_without_a_winner(lib, R, Hd, V):
+    from synth import make_lmhead_case
+    c = make_lmhead_case(R + Hd + V, R, Hd, V, plant=False)
+    tok, logits = run(lib, c)
+    check_against_oracle(c, tok, logits, exact_tokens=False)
+
+
+def test_duplicated_maximum_returns_lowest_index(lib):
+    from synth import make_lmhead_case
+    c = make_lmhead_case(5, 32, 512, 9000, dup_rows=32)
+    tok, logits = run(lib, c)
+    assert np.array_equal(tok, c.targets)
+    rows = np.arange(32)
+    assert np.all(np.count_nonzero(logits == logits[rows, tok][:, None], axis=1) >= 2)
+
+
+def test_qwen3_8b_vocabulary_full_size(lib):
+    """The 8B shape: 32 rows, hidden 4096, vocabulary 151936 (1.24 GB of weights)."""
+    from synth import make_lmhead_case
+    c = make_lmhead_case(8, 32, 4096, 151936)
+    tok, logits = run(lib, c)
+    check_against_oracle(c, tok, logits, exact_tokens=True)
+    tok2, _ = run(lib, c, with_logits=False)          # the fast path gives the same tokens
+    assert np.array_equal(tok, tok2)
+
+
+@pytest.mark.parametrize("n_acc", [0, 3, 31, 32])
+def test_lmhead_accept_matches_oracle(lib, n_acc):
+    from oracle import accept
+    from synth import make_lmhead_case
+    B, K, Hd, V = 2, 32, 1024, 30000
+    c = make_lmhead_case(100 + n_acc, B * K, Hd, V)
+    a = c.targets.reshape(B, K)
+    d = a.copy()
+    for b in range(B):
+        if n_acc < K:
+            d[b, n_acc] = (a[b, n_acc] + 1) % V
+    h = bf16_dev(c.hidden).view(B, K, Hd)
+    w = bf16_dev(c.weight)
+    outs = [torch.full(s, -7, dtype=torch.int32, device="cuda") for s in ((B, K), (B,), (B,), (B,))]
+    lib.orthrus_lmhead_accept(h, w, i32_dev(d), *outs)
+    torch.cuda.synchronize()
+    ar, na, ne, nx = (t.cpu().numpy() for t in outs)
+    ref_na, ref_ne, ref_nx = accept(d, a)
+    assert np.array_equal(ar, a)
+    assert np.array_equal(na, ref_na) and np.array_equal(ne, ref_ne) and np.array_equal(nx, ref_nx)
+    assert np.all(na == n_acc)
