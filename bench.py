@@ -216,6 +216,21 @@ def main():
         "commit": lambda i: dv.orthrus_commit_kv(kvs[(2 * i + 1) % n_pools], kb_commit, vb_commit, n_emit,
                                                  lens_out, stream=None),
     }
+    # fused LM head + argmax (the logits-free consensus), at the model's
+    # hidden size: weights N(0, 0.02) and hidden states N(0, 1), bf16, drawn
+    # on the device from a seeded generator (1.24 GB of weights at the 8B
+    # shape, far more than the Infinity Cache)
+    Hd = w["hidden"]
+    lm_bytes = V * Hd * 2 + B * K * Hd * 2 + B * K * 4
+    if not args.quick:
+        gen = torch.Generator(device=dev).manual_seed(w["seed"] + 7)
+        lm_w = torch.randn((V, Hd), generator=gen, device=dev).mul_(0.02).to(torch.bfloat16)
+        lm_h = torch.randn((B, K, Hd), generator=gen, device=dev).to(torch.bfloat16)
+        ws_lm = dv.lmhead_workspace(B * K, Hd, V, dev)
+        op_calls["lmhead_argmax"] = lambda i: dv.orthrus_lmhead_argmax(lm_h, lm_w, d_tok, workspace=ws_lm,
+                                                                       stream=None)
+        op_calls["lmhead_accept"] = lambda i: dv.orthrus_lmhead_accept(lm_h, lm_w, d_tok, a_tok, n_acc, n_emit,
+                                                                       nxt, workspace=ws_lm, stream=None)
     op_ms, op_min = {}, {}
     for op, call in ([] if args.quick else op_calls.items()):
         graph = capture(lambda call=call: [call(i) for i in range(REPS)])
@@ -282,6 +297,15 @@ def main():
             "mfma_tflops": round(attn_flops / dom_s / 1e12, 1),
             "mfma_frac": round(attn_flops / dom_s / 1e12 / BF16_PEAK_TFLOPS, 4),
         },
+    }
+    lm_s = op_ms["lmhead_argmax"] * 1e-3
+    res["lmhead"] = {
+        "config": {"rows": B * K, "hidden": Hd, "vocab": V},
+        "op_ms": {o: round(op_ms[o], 4) for o in ("lmhead_argmax", "lmhead_accept")},
+        "roofline": {"kernel": "lmhead_kernel + argmax_final_kernel (one ABI call)", "bound": "hbm",
+                     "achieved": round(lm_bytes / lm_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(lm_bytes / lm_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": lm_bytes},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, case, (qv, kbv, vbv), cons, kv_bytes)

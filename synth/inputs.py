@@ -369,16 +369,16 @@ __all__ += ["LmHeadCase", "make_lmhead_case"]
 WORKLOADS = {
     # tiny CPU-checkable case
     "tiny": dict(seed=1, B=1, K=8, Hq=2, Hkv=1, D=64, seq_lens=[256], V=1024,
-                 accept="uniform"),
+                 accept="uniform", hidden=128),
     # Qwen3-8B attention shape, 4K context
     "qwen3_8b_4k": dict(seed=2, B=1, K=32, Hq=32, Hkv=8, D=128, seq_lens=[4096],
-                        V=151936, accept="geometric"),
+                        V=151936, accept="geometric", hidden=4096),
     # same shape at 40960-token context
     "qwen3_8b_40k": dict(seed=3, B=1, K=32, Hq=32, Hkv=8, D=128, seq_lens=[40960],
-                         V=151936, accept="geometric"),
+                         V=151936, accept="geometric", hidden=4096),
     # batched ragged serving step, 16 sequences, L_b ~ U[1024, 32768]
     "qwen3_8b_ragged16": dict(seed=4, B=16, K=32, Hq=32, Hkv=8, D=128, seq_lens=None,
-                              V=151936, accept="geometric"),
+                              V=151936, accept="geometric", hidden=4096),
 }
 
 
