@@ -39,6 +39,7 @@ struct ArgmaxPlan {
 constexpr int kLmWorkgroups = 256;
 constexpr int kLmRowChunk = 32;
 constexpr int kLmKTile = 64;
+constexpr int kLmRegHidden = 5120;   // up to this hidden size the query rows live in registers
 
 struct LmHeadPlan {
   int rows = 0, hidden = 0, V = 0;

@@ -68,6 +68,26 @@ static_assert(KT == 64, "8 granules of 16 bytes per tile row");
 // rows one MFMA operand read touches fall on distinct LDS banks.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
+// Per-lane best keys (query row col; lanes l and l^32 hold the same row) ->
+// one key per row for the whole workgroup, written to keys[row][wg].  red is
+// 2 KiB of LDS that no wavefront uses any more.
+__device__ __forceinline__ void write_row_keys(const LmArgs& a, unsigned long long best, unsigned long long* red,
+                                               int wg, int row0, int wave, int half, int col) {
+  const auto lo = __builtin_amdgcn_permlane32_swap(uint32_t(best), uint32_t(best), false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap(uint32_t(best >> 32), uint32_t(best >> 32), false, false);
+  best = umax64((static_cast<unsigned long long>(hi[0]) << 32) | lo[0],
+                (static_cast<unsigned long long>(hi[1]) << 32) | lo[1]);
+  if (half == 0) red[wave * 32 + col] = best;
+  __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): the LDS writes are done
+  lds_barrier();
+  if (wave == 0 && half == 0 && row0 + col < a.rows) {
+    unsigned long long k = red[col];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) k = umax64(k, red[w * 32 + col]);
+    a.keys[size_t(row0 + col) * a.nwg + wg] = k;
+  }
+}
+
 __global__ __launch_bounds__(512, 1) void lmhead_kernel(LmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ring[NS * STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t sink[512];   // target of the spare loads
@@ -156,26 +176,129 @@ __global__ __launch_bounds__(512, 1) void lmhead_kernel(LmArgs a) {
     }
   }
 
-  // lanes l and l^32 cover the same query row: combine, then across wavefronts
-  {
-    const auto lo = __builtin_amdgcn_permlane32_swap(uint32_t(best), uint32_t(best), false, false);
-    const auto hi = __builtin_amdgcn_permlane32_swap(uint32_t(best >> 32), uint32_t(best >> 32), false, false);
-    const unsigned long long k0 = (static_cast<unsigned long long>(hi[0]) << 32) | lo[0];
-    const unsigned long long k1 = (static_cast<unsigned long long>(hi[1]) << 32) | lo[1];
-    best = umax64(k0, k1);
-  }
   wait_vmcnt<0>();                        // trailing zero-tile loads have landed
   lds_barrier();                          // every wavefront is done with the ring
-  unsigned long long* red = reinterpret_cast<unsigned long long*>(ring);   // [8][32]
-  if (half == 0) red[wave * 32 + col] = best;
-  __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): the LDS writes are done
-  lds_barrier();
-  if (wave == 0 && half == 0 && row0 + col < a.rows) {
-    unsigned long long k = red[col];
+  write_row_keys(a, best, reinterpret_cast<unsigned long long*>(ring), wg, row0, wave, half, col);
+}
+
+// Row-streaming variant for hidden <= kLmRegHidden (the query rows fit in
+// registers).  A tile is 32 vocabulary rows x 512 hidden elements: every
+// weight row contributes 1 KiB of consecutive memory, fetched by one load
+// instruction (64 lanes x 16 bytes), so HBM sees long runs instead of the
+// 128-byte pieces of the tile above.  Wavefront w takes hidden elements
+// 64w .. 64w+63 of every tile; its query-row operands for all tiles are
+// loaded once into registers.  After the last tile of a block of 32
+// vocabulary rows the 8 wavefronts' partial sums meet in LDS and are added in
+// wavefront order (a fixed order: the logits do not depend on the launch).
+constexpr int R2_KT = 512;                     // hidden elements per tile
+constexpr int R2_NS = 5;                       // ring stages
+constexpr int R2_TILE = 32 * R2_KT;            // 32 KiB
+constexpr int R2_LPT = 4;                      // loads per wavefront per tile: 4 rows of 1 KiB
+constexpr int R2_MAX_KT = kLmRegHidden / R2_KT;
+
+__global__ __launch_bounds__(512, 1) void lmhead_rows_kernel(LmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t ring[R2_NS * R2_TILE];
+  static_assert(8 * 32 * 32 * 4 == R2_TILE * 2, "a block's partial sums fill one stage");
+  const int wg = blockIdx.x;
+  const int row0 = blockIdx.y * RC;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int v0 = int((int64_t(a.V) * wg) / a.nwg);
+  const int v1 = int((int64_t(a.V) * (wg + 1)) / a.nwg);
+  const int nkt = (a.hidden + R2_KT - 1) / R2_KT;
+  const int ntiles = ((v1 - v0 + 31) / 32) * nkt;
+
+  // query row col, hidden elements kt*512 + 64 wave + 16 ks + 8 half + 0..7
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 hreg[R2_MAX_KT][4];
+  {
+    const bool row_ok = row0 + col < a.rows;
 #pragma unroll
-    for (int w = 1; w < 8; ++w) k = umax64(k, red[w * 32 + col]);
-    a.keys[size_t(row0 + col) * a.nwg + wg] = k;
+    for (int kt = 0; kt < R2_MAX_KT; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int k = kt * R2_KT + wave * 64 + ks * 16 + half * 8;
+        hreg[kt][ks] = u32x4{0u, 0u, 0u, 0u};
+        if (kt < nkt && row_ok && k < a.hidden)
+          hreg[kt][ks] = *reinterpret_cast<const u32x4*>(a.h + size_t(row0 + col) * a.hidden + k);
+      }
   }
+  wait_vmcnt<0>();                       // nothing but tile loads is in flight in the loop
+
+  // Tile t: block t / nkt, hidden tile t % nkt.  Wavefront w loads rows
+  // 4w .. 4w+3 of the block, one 1 KiB instruction each; lane l fetches
+  // granule l ^ (row % 16) so that granule c of a row sits at c ^ (row % 16).
+  auto issue_tile = [&](int t, uint16_t* st) {
+    const int blk = t / nkt;
+    const int kt = t - blk * nkt;
+    const bool live = t < ntiles;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wave * 4 + i;
+      const int v = v0 + blk * 32 + r;
+      const int c = lane ^ (r & 15);
+      const int k = kt * R2_KT + c * 8;
+      const void* src = (live && v < v1 && k < a.hidden)
+                            ? static_cast<const void*>(a.w + size_t(v) * a.hidden + k)
+                            : static_cast<const void*>(g_lm_zero16);
+      load_lds16(src, lds_addr(st + r * R2_KT));
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < R2_NS - 1; ++k) issue_tile(k, ring + k * R2_TILE);
+
+  f32x16 acc = f32x16{};
+  unsigned long long best = 0ull;        // best key of query row col over this lane's vocabulary
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmcnt<(R2_NS - 2) * R2_LPT>();  // tile t has landed for this wavefront
+    lds_barrier();                       // ... for every wavefront; stage of t-1 is free
+    const int tn = t + R2_NS - 1;
+    issue_tile(tn, ring + (tn % R2_NS) * R2_TILE);
+    const uint16_t* wt = ring + (t % R2_NS) * R2_TILE;
+    const int blk = t / nkt;
+    const int kt = t - blk * nkt;
+#pragma unroll
+    for (int kk = 0; kk < R2_MAX_KT; ++kk) {
+      if (kk != kt) continue;            // uniform: pick this tile's register operands
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int g = wave * 8 + ks * 2 + half;   // granule of the row holding this lane's 8 elements
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(wt + col * R2_KT + ((g ^ (col & 15)) * 8));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, hreg[kk][ks]), acc, 0, 0, 0);
+      }
+    }
+    if (kt == nkt - 1) {                 // uniform: the block's partial sums are complete
+      // They meet in the stage of tile t, which no load targets before the
+      // next step's barrier.  lane l, value v: vocabulary row 8(v/4) + 4 half
+      // + v%4 of the block, query row col.
+      float* red = reinterpret_cast<float*>(ring + (t % R2_NS) * R2_TILE);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's reads of the stage are done
+      lds_barrier();                       // ... and every other wavefront's
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[(wave * 32 + 8 * (v >> 2) + 4 * half + (v & 3)) * 32 + col] = acc[v];
+      acc = f32x16{};
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): partial sums written
+      lds_barrier();
+      // wavefront w adds up vocabulary rows 4w + 2 half + {0, 1} for query row col
+      const bool row_ok = row0 + col < a.rows;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = wave * 4 + 2 * half + e;
+        float sum = red[i * 32 + col];
+#pragma unroll
+        for (int w = 1; w < 8; ++w) sum += red[(w * 32 + i) * 32 + col];
+        const int vi = v0 + blk * 32 + i;
+        if (vi < v1) {
+          best = umax64(best, make_key(sum, vi));
+          if (a.logits && row_ok) a.logits[size_t(row0 + col) * a.V + vi] = sum;
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();                        // trailing zero-tile loads have landed
+  lds_barrier();                          // every wavefront is done with the ring and red
+  write_row_keys(a, best, reinterpret_cast<unsigned long long*>(ring), wg, row0, wave, half, col);
 }
 
 }  // namespace
@@ -184,6 +307,8 @@ hipError_t launch_lmhead(const LmHeadPlan& p, const void* hidden, const void* we
                          void* ws, hipStream_t stream) {
   LmArgs a{static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(weight), logits,
            static_cast<unsigned long long*>(ws), p.rows, p.hidden, p.V, p.nwg};
+  if (p.hidden <= kLmRegHidden)
+    return launch_kernel(&lmhead_rows_kernel, dim3(p.nwg, p.nrc), dim3(512), stream, a);
   return launch_kernel(&lmhead_kernel, dim3(p.nwg, p.nrc), dim3(512), stream, a);
 }
 

@@ -51,8 +51,11 @@ def check_against_oracle(c, tok, logits, exact_tokens):
         assert np.array_equal(tok, lm_argmax(c.hidden, c.weight))
 
 
+# hidden <= 5120 runs the row-streaming kernel (query rows in registers),
+# larger hidden sizes the tile kernel that stages them in LDS
 @pytest.mark.parametrize("R,Hd,V", [(32, 256, 5000), (7, 128, 777), (1, 64, 1), (40, 128, 3000),
-                                    (32, 4096, 20011), (3, 64, 10), (65, 192, 300)])
+                                    (32, 4096, 20011), (3, 64, 10), (65, 192, 300), (9, 5120, 700),
+                                    (8, 8192, 3000), (5, 5184, 1000), (33, 576, 2049)])
 def test_planted_winner(lib, R, Hd, V):
     from synth import make_lmhead_case
     c = make_lmhead_case(R * 31 + V, R, Hd, V)
