@@ -56,6 +56,9 @@ def parse_args():
                    help="timed steps only (no per-op breakdown, no CPU baseline): for profiler runs")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    p.add_argument("--e2e", action="store_true",
+                   help="only time whole decode steps of the Qwen3-8B-shaped model (greedy vs Orthrus)")
+    p.add_argument("--e2e-contexts", default="4096,40960")
     return p.parse_args()
 
 
@@ -119,6 +122,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": a.numel() * 4,
                           "copy_calibration_bytes_written": b.numel() * 4}))
+        return
+
+    if args.e2e:
+        print(json.dumps(e2e(args, torch, dv, synth)), flush=True)
         return
 
     w, case, (qv, kbv, vbv), cons = setup(args, torch, dv, synth)
@@ -310,6 +317,66 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, case, (qv, kbv, vbv), cons, kv_bytes)
     print(json.dumps(res), flush=True)
+
+
+def e2e(args, torch, dv, synth):
+    """Whole decode steps of the Qwen3-8B-shaped model (36 layers, random bf16
+    weights, all layers' KV cache filled with N(0,1) values to the given
+    context): one greedy step (1 row) against one Orthrus step (draft pass of K
+    rows, fused LM-head argmax, verify pass, fused LM-head acceptance, commit),
+    each replayed from a HIP graph.  Tokens per second of the Orthrus loop are
+    given for mean emitted lengths 5.39 (the pages' reported mean) and 6.63
+    (geometric(0.15) acceptance); acceptance changes only the commit size."""
+    from dual_view_draft_amd.model import DualViewModel, ModelCache
+    cfg, K = synth.QWEN3_8B, 32
+    dev = torch.device("cuda:0")
+    model = DualViewModel(cfg, synth.make_model_weights_device(8, cfg, dev), max_block=K)
+    res = {"e2e": "qwen3_8b_shape", "layers": cfg.layers, "hidden": cfg.hidden, "vocab": cfg.vocab,
+           "block_k": K, "timing": "HIP graph replay", "contexts": []}
+    reps = 10
+    for L in (int(x) for x in args.e2e_contexts.split(",")):
+        cache = ModelCache(cfg, L + (4 * reps + 8) * K + 256, dev)
+        cache.fill_random(L)
+        tok = torch.zeros(1, dtype=torch.int64, device=dev)
+        out = torch.zeros(1, dtype=torch.int32, device=dev)
+        anchor = torch.zeros(1, dtype=torch.int64, device=dev)
+        d, a = (torch.zeros((1, K), dtype=torch.int32, device=dev) for _ in range(2))
+        n_acc, n_emit, nxt = (torch.zeros(1, dtype=torch.int32, device=dev) for _ in range(3))
+
+        def greedy2():
+            for _ in range(2):                 # two steps: the length buffers return to their roles
+                model.greedy_step(cache, tok, out)
+
+        def orthrus2():
+            for _ in range(2):
+                model.orthrus_step(cache, anchor, K, d, a, n_acc, n_emit, nxt)
+
+        times = {}
+        for name, fn in (("greedy_step_ms", greedy2), ("orthrus_step_ms", orthrus2)):
+            fn()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fn()
+            graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times[name] = e0.elapsed_time(e1) / (2 * reps)
+        tg, to = times["greedy_step_ms"], times["orthrus_step_ms"]
+        res["contexts"].append({
+            "context": L, "greedy_step_ms": round(tg, 3), "orthrus_step_ms": round(to, 3),
+            "greedy_tokens_per_s": round(1e3 / tg, 1),
+            "orthrus_tokens_per_s": {str(e): round(e * 1e3 / to, 1) for e in (5.39, 6.63)},
+            "speedup_vs_greedy": {str(e): round(e * tg / to, 2) for e in (5.39, 6.63)},
+            "break_even_tokens_per_step": round(to / tg, 2)})
+        del cache
+        torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(args, case, vqkv, cons, kv_bytes):

@@ -25,7 +25,8 @@ import numpy as np
 __all__ = [
     "BF16_NAN", "BF16_SENTINEL", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "PagedCase", "make_paged_case", "make_block_qkv", "ConsensusCase", "make_consensus_case",
-    "draw_accept_lengths", "make_tie_logits", "ToyConfig", "TOY_CFG5",
+    "draw_accept_lengths", "make_tie_logits", "ToyConfig", "TOY_CFG5", "QWEN3_8B",
+    "make_model_weights_device",
     "TOY_TINY", "make_toy_weights", "make_prompt", "WORKLOADS",
 ]
 
@@ -276,6 +277,10 @@ class ToyConfig:
 
 TOY_CFG5 = ToyConfig(layers=4, hidden=1024, Hq=16, Hkv=4, D=64, ffn=2816,
                      vocab=32000, rope_base=1e6)
+# Qwen3-8B shape (36 layers, hidden 4096, 32/8 heads of 128, SwiGLU 12288,
+# vocabulary 151936): random weights only, for timing the whole step
+QWEN3_8B = ToyConfig(layers=36, hidden=4096, Hq=32, Hkv=8, D=128, ffn=12288,
+                     vocab=151936, rope_base=1e6)
 TOY_TINY = ToyConfig(layers=2, hidden=64, Hq=4, Hkv=2, D=16, ffn=96,
                      vocab=97, rope_base=1e4, weight_std=0.3)
 
@@ -308,6 +313,35 @@ def make_toy_weights(seed: int, cfg: ToyConfig) -> dict:
         w[p + "wk_diff"] = _normal_bf16(rng, (H, Hkv * D), s)
         w[p + "wv_diff"] = _normal_bf16(rng, (H, Hkv * D), s)
         w[p + "wo_diff"] = _normal_bf16(rng, (Hq * D, H), s)
+    return w
+
+
+def make_model_weights_device(seed: int, cfg: ToyConfig, device) -> dict:
+    """The same set of weights as make_toy_weights, drawn on the GPU (bf16
+    torch tensors; tens of GB at the 8B shape are impractical to draw on the
+    host).  Matrices are [in, out] except the LM head, [vocab, hidden] (row v =
+    token v); q/k/v projections come fused as one [hidden, (Hq + 2 Hkv) D]
+    matrix per view, gate and up as one [hidden, 2 ffn] matrix."""
+    import torch
+    gen = torch.Generator(device=device).manual_seed(seed)
+    H, Hq, Hkv, D, F = cfg.hidden, cfg.Hq, cfg.Hkv, cfg.D, cfg.ffn
+    s = cfg.weight_std
+
+    def normal(*shape):
+        return torch.randn(shape, generator=gen, device=device).mul_(s).to(torch.bfloat16)
+
+    ones = lambda n: torch.ones(n, dtype=torch.bfloat16, device=device)  # noqa: E731
+    w = {"embed": normal(cfg.vocab + 1, H), "final_norm": ones(H), "lm_head": normal(cfg.vocab, H)}
+    for i in range(cfg.layers):
+        p = f"l{i}."
+        w[p + "attn_norm"], w[p + "ffn_norm"] = ones(H), ones(H)
+        w[p + "q_norm"], w[p + "k_norm"] = ones(D), ones(D)
+        w[p + "wqkv"] = normal(H, (Hq + 2 * Hkv) * D)
+        w[p + "wo"] = normal(Hq * D, H)
+        w[p + "w_gate_up"] = normal(H, 2 * F)
+        w[p + "w_down"] = normal(F, H)
+        w[p + "wqkv_diff"] = normal(H, (Hq + 2 * Hkv) * D)
+        w[p + "wo_diff"] = normal(Hq * D, H)
     return w
 
 

@@ -1,0 +1,69 @@
+"""End-to-end losslessness at the Qwen3-8B shape on the GPU: 36 layers, hidden
+4096, 32/8 heads of 128, SwiGLU 12288, vocabulary 151936, random bf16 weights
+N(0, 0.02) with a random diffusion module per layer (about 19 GB), bf16
+matrix products with fp32 accumulation.  The Orthrus loop must emit exactly
+the tokens of plain greedy decoding of the same model: with its own
+(untrained) drafter, with a teacher drafter that proposes the greedy
+continuation corrupted at a geometric position, and with a drafter that is
+always wrong."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+PROMPT, N_NEW, K = 80, 48, 32
+
+
+@pytest.fixture(scope="module")
+def setup():
+    import dual_view_draft_amd as dv
+    from dual_view_draft_amd.model import DualViewModel
+    from synth import QWEN3_8B, make_model_weights_device, make_prompt
+    dv.load_library()
+    cfg = QWEN3_8B
+    model = DualViewModel(cfg, make_model_weights_device(8, cfg, "cuda"), max_block=K)
+    prompt = torch.from_numpy(make_prompt(8, PROMPT, cfg.vocab)).cuda()
+    ref, secs = model.greedy(prompt, N_NEW + K)          # extra tokens for the teacher drafter
+    print(f"greedy: {len(ref)} tokens, {secs:.2f} s (eager launches)", flush=True)
+    return model, prompt, ref
+
+
+def test_greedy_is_not_degenerate(setup):
+    _, _, ref = setup
+    assert len(set(ref[:N_NEW])) > 10
+
+
+def test_orthrus_own_drafter_matches_greedy(setup):
+    model, prompt, ref = setup
+    toks, emits, _ = model.orthrus(prompt, 16, K)
+    assert toks == ref[:16]
+    assert min(emits) >= 1
+
+
+def test_orthrus_teacher_drafter_matches_greedy(setup):
+    model, prompt, ref = setup
+    rng = np.random.default_rng(3)
+    V = model.cfg.vocab
+
+    def teacher(out, k):
+        e = len(out)
+        d = np.array(ref[e:e + k], dtype=np.int32)
+        m = min(int(rng.geometric(0.15)) - 1, k)
+        if m < k:
+            d[m] = (d[m] + 1) % V
+        return d
+
+    toks, emits, _ = model.orthrus(prompt, N_NEW, K, drafter=teacher)
+    print(f"teacher drafter: {len(emits)} steps, mean emitted {np.mean(emits):.2f}", flush=True)
+    assert toks == ref[:N_NEW]
+    assert len(emits) < N_NEW // 2
+
+
+def test_orthrus_wrong_drafter_matches_greedy(setup):
+    model, prompt, ref = setup
+    V = model.cfg.vocab
+    toks, emits, _ = model.orthrus(prompt, 12, K,
+                                   drafter=lambda out, k: (np.array(ref[len(out):len(out) + k]) + 1) % V)
+    assert toks == ref[:12]
+    assert emits == [1] * 11
