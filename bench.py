@@ -241,9 +241,10 @@ def main():
     op_ms, op_min = {}, {}
     for op, call in ([] if args.quick else op_calls.items()):
         graph = capture(lambda call=call: [call(i) for i in range(REPS)])
-        graph.replay()
+        for _ in range(3):                         # settle clocks and caches before timing
+            graph.replay()
         samples = []
-        for _ in range(5):
+        for _ in range(7):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             graph.replay()
