@@ -11,8 +11,9 @@ one is the gist.science technical summary of "Orthrus: Memory-Efficient
 Parallel Token Generation via Dual-View Diffusion" (written in Dutch), cited
 below as [gist §x].  The co-author's post #21 in the Hacker News thread
 "Orthrus-Qwen3: up to 7.8x tokens/forward on Qwen3, identical output
-distribution" is cited as [HN #21] (post #26 of the same thread as [HN #26]).  The paper abstract (codewithpapers and
-fugumt pages) is cited as [abstract].
+distribution" is cited as [HN #21] (post #26 of the same thread as
+[HN #26]).  The paper abstract (codewithpapers and fugumt pages) is cited as
+[abstract], the author profile page as [profile].
 
 Modules:
   attention  - page-table gather + dense masked softmax attention (draft mask,
@@ -20,6 +21,9 @@ Modules:
   consensus  - vocabulary argmax, longest-prefix acceptance, cache commit
   lmhead     - LM-head projection of the final hidden states and the greedy
                token of every row
+  fp8        - an e4m3 KV cache: the format, quantisation with per-head
+               scales, and attention over the decoded values (a stated
+               reading; the pages describe no quantised cache)
   toy        - a tiny fp64 Qwen3-style decoder with a diffusion view, the
                Orthrus loop and plain greedy decoding
 
