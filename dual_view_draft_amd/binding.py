@@ -19,6 +19,9 @@ _lib = None
 
 ORTHRUS_PAGE_SIZE = 16
 ORTHRUS_MAX_BLOCK = 64
+ORTHRUS_KV_BF16 = 0
+ORTHRUS_KV_FP8_E4M3 = 1
+_FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)   # e4m3 codes, raw or typed
 
 
 class OrthrusError(RuntimeError):
@@ -35,7 +38,8 @@ class orthrus_kv(ctypes.Structure):
                 ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
                 ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("max_pages_per_seq", ctypes.c_int32)]
+                ("max_pages_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 EXPORTS = {
@@ -64,6 +68,7 @@ EXPORTS = {
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_void_p, ctypes.c_void_p]),
+    "orthrus_quantize_kv": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3),
 }
 EXPORTS["orthrus_attn_verify"] = EXPORTS["orthrus_attn_draft"]
 
@@ -112,23 +117,39 @@ def _stream(stream):
 class PagedKV:
     """One layer's view of the shared paged cache (tensors, device memory).
 
-    k_pages, v_pages: bf16 [num_pages, Hkv, 16, D]; block_table: int32
+    k_pages, v_pages: [num_pages, Hkv, 16, D], bf16, or e4m3 codes (uint8 or
+    float8_e4m3fn) with k_scale, v_scale fp32 [Hkv]; block_table: int32
     [B, max_pages]; seq_lens: int32 [B]."""
     k_pages: torch.Tensor
     v_pages: torch.Tensor
     block_table: torch.Tensor
     seq_lens: torch.Tensor
+    k_scale: torch.Tensor | None = None
+    v_scale: torch.Tensor | None = None
+
+    @property
+    def is_fp8(self) -> bool:
+        return self.k_pages.dtype in _FP8_DTYPES
 
     def c_struct(self) -> orthrus_kv:
-        for t, dt in ((self.k_pages, torch.bfloat16), (self.v_pages, torch.bfloat16),
-                      (self.block_table, torch.int32), (self.seq_lens, torch.int32)):
+        elem = self.k_pages.dtype if self.is_fp8 else torch.bfloat16
+        for t, dt in ((self.v_pages, elem), (self.block_table, torch.int32), (self.seq_lens, torch.int32)):
             if t.dtype != dt:
                 raise ValueError(f"expected {dt}, got {t.dtype}")
+        if self.k_pages.dtype != elem:
+            raise ValueError(f"k_pages must be bfloat16 or e4m3 codes, got {self.k_pages.dtype}")
         n, hkv, p, d = self.k_pages.shape
         if tuple(self.v_pages.shape) != (n, hkv, p, d):
             raise ValueError("k_pages and v_pages shapes differ")
+        # the library rejects an e4m3 cache without scales where it reads
+        # values (attention); the commit copies codes and needs none
+        for t in (self.k_scale, self.v_scale):
+            if t is not None and (t.dtype != torch.float32 or t.numel() != hkv):
+                raise ValueError("k_scale and v_scale must be float32 with num_kv_heads entries")
+        scales = (_ptr(self.k_scale), _ptr(self.v_scale)) if self.is_fp8 else (None, None)
         return orthrus_kv(_ptr(self.k_pages), _ptr(self.v_pages), _ptr(self.block_table),
-                          _ptr(self.seq_lens), n, p, hkv, d, self.block_table.shape[1])
+                          _ptr(self.seq_lens), n, p, hkv, d, self.block_table.shape[1],
+                          ORTHRUS_KV_FP8_E4M3 if self.is_fp8 else ORTHRUS_KV_BF16, *scales)
 
     @property
     def head_dim(self) -> int:
@@ -289,7 +310,8 @@ def orthrus_lmhead_accept(hidden_states: torch.Tensor, weight: torch.Tensor, dra
 def orthrus_commit_kv(kv_layer0: PagedKV, k_blk: torch.Tensor, v_blk: torch.Tensor,
                       n_emit: torch.Tensor, seq_lens_out: torch.Tensor, *,
                       pool_layer_stride: int = 0, stream=None):
-    """Append the accepted rows' K/V (k_blk, v_blk: bf16 [layers,B,K,Hkv,D]) to the cache.
+    """Append the accepted rows' K/V (k_blk, v_blk: [layers,B,K,Hkv,D] in the
+    cache's element type) to the cache.
 
     kv_layer0 describes layer 0's pools; layer l's pools start pool_layer_stride
     elements later (pass the stride of a [layers, num_pages, Hkv, 16, D] pool)."""
@@ -300,3 +322,24 @@ def orthrus_commit_kv(kv_layer0: PagedKV, k_blk: torch.Tensor, v_blk: torch.Tens
                                           _ptr(k_blk), _ptr(v_blk), int(blk_stride), _ptr(n_emit),
                                           B, K, _ptr(seq_lens_out), _stream(stream))
     _check(rc, "orthrus_commit_kv")
+
+
+def orthrus_quantize_kv(k: torch.Tensor, v: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                        k_out: torch.Tensor, v_out: torch.Tensor, *, stream=None):
+    """e4m3 codes of bf16 K and V rows [..., Hkv, D] with per-head fp32 scales
+    (k_out, v_out: uint8 or float8_e4m3fn of the same shape)."""
+    if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("k and v must be bfloat16")
+    if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32:
+        raise ValueError("scales must be float32")
+    if k_out.dtype not in _FP8_DTYPES or v_out.dtype not in _FP8_DTYPES:
+        raise ValueError("k_out and v_out must be uint8 or float8_e4m3fn")
+    if k.shape != v.shape or k_out.shape != k.shape or v_out.shape != k.shape:
+        raise ValueError("k, v, k_out and v_out must have one shape")
+    Hkv, D = k.shape[-2], k.shape[-1]
+    if k_scale.numel() != Hkv or v_scale.numel() != Hkv:
+        raise ValueError("one scale per KV head")
+    rows = k.numel() // (Hkv * D)
+    rc = load_library().orthrus_quantize_kv(_ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), rows, Hkv, D,
+                                            _ptr(k_out), _ptr(v_out), _stream(stream))
+    _check(rc, "orthrus_quantize_kv")

@@ -188,4 +188,19 @@ int orthrus_commit_kv(const orthrus_kv* kv, int num_layers, int64_t pool_layer_s
   }
 }
 
+int orthrus_quantize_kv(const void* k, const void* v, const float* k_scale, const float* v_scale, int rows,
+                        int num_kv_heads, int head_dim, void* k_out, void* v_out, void* stream) {
+  try {
+    std::string err;
+    const int rc = orthrus::check_quantize(k, v, k_scale, v_scale, rows, num_kv_heads, head_dim, k_out,
+                                           v_out, &err);
+    if (rc != ORTHRUS_OK) return fail(rc, err);
+    if (rows == 0) return ORTHRUS_OK;
+    return hip_status(orthrus::launch_quantize_kv(k, v, k_scale, v_scale, rows, num_kv_heads, head_dim, k_out,
+                                                  v_out, as_stream(stream)));
+  } catch (...) {
+    return fail(ORTHRUS_ERR_HIP, "internal error");
+  }
+}
+
 }  // extern "C"

@@ -55,22 +55,27 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 typedef const int32_t __attribute__((address_space(4)))* cptr_i32;
+typedef const float __attribute__((address_space(4)))* cptr_f32;
 typedef const void __attribute__((address_space(1)))* gptr_void;
 typedef void __attribute__((address_space(3)))* lptr_void;
 typedef bf16x4 __attribute__((address_space(3)))* lptr_bf16x4;
+typedef i32x2 __attribute__((address_space(3)))* lptr_i32x2;
 
 // 16 zero bytes: the source of tile rows past the last key.
 __device__ __attribute__((aligned(16))) uint16_t g_zero16[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 
 struct AttnArgs {
-  const uint16_t* k_pages;
-  const uint16_t* v_pages;
+  const void* k_pages;   // bf16 or e4m3 [num_pages][Hkv][16][D]
+  const void* v_pages;
   const int32_t* block_table;
   const int32_t* seq_lens;
+  const float* k_scale;   // e4m3 cache: [Hkv]
+  const float* v_scale;
   const uint16_t* q;
-  const uint16_t* k_blk;
-  const uint16_t* v_blk;
+  const void* k_blk;     // same element type as the pages
+  const void* v_blk;
   uint16_t* part_o;  // [B][Hkv][nchunks][nsplit][rpc][D] bf16: O / l of the split
   float* part_ml;    // [B][Hkv][nchunks][nsplit][rpc][2]: m (log2 units), l
   int B, K, Hq, Hkv, G, num_pages, maxp, max_ctx, split, nsplit, rows, nchunks, rpc;
@@ -111,34 +116,55 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
+// Tile geometry of the split kernel for head_dim D and the cache's element
+// type (bf16, or e4m3 bytes when FP8).
+template <int D, bool FP8>
 struct SplitCfg {
-  static constexpr int KG = D / 8;                 // 16-byte granules per key/value row
-  static constexpr int NS = 5;                     // LDS ring stages
-  static constexpr int TILE_ELEMS = kTile * D;     // bf16 values per K (or V) tile
-  static constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;
-  static constexpr int RPI = 512 / D;              // tile rows per 1 KiB wave-wide LDS load
+  static constexpr int RB = FP8 ? D : 2 * D;       // bytes per key/value row
+  static constexpr int KG = RB / 16;               // 16-byte granules per row
+  static constexpr int NS = FP8 ? 9 : 5;           // LDS ring stages
+  static constexpr int TILE_BYTES = kTile * RB;    // one K (or V) tile
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  static constexpr int RPI = 1024 / RB;            // tile rows per 1 KiB wave-wide LDS load
   static constexpr int LPR = 8 / RPI;              // such loads per 8 rows of one tensor
   static constexpr int LPT = 2 * LPR;              // loads per wavefront per tile (K and V)
+  static_assert(LPR >= 1, "a wavefront's 8 rows fill at least one 1 KiB load");
+
+  // Physical 16-byte granule of logical granule c in tile row t is c ^ swizzle(t).
+  // K: the 16 rows read by 16 consecutive lanes (one per row, same logical
+  // granule) land on distinct LDS banks.  V: granule pairs stay together (the
+  // transposing reads take 8 or 16 bytes of one pair) and the rows that one
+  // transposing read gathers land on distinct banks.
+  __device__ static __forceinline__ int kswz(int t) { return FP8 ? (t >> 1) & 7 : t & (KG - 1); }
+  __device__ static __forceinline__ int vswz(int t) {
+    return FP8 ? 2 * (((t >> 1) & 1) | ((t >> 2) & 2)) : 2 * (t & (KG / 2 - 1));
+  }
 };
 
-template <int D, bool VERIFY>
+// Eight e4m3 codes (two dwords, lowest byte first) -> eight bf16 values.
+// Every e4m3 value is exactly representable in bf16; the scale operand of the
+// conversion is 1, so this is a pure change of format.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int D, bool VERIFY, bool FP8>
 __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
-  using C = SplitCfg<D>;
-  constexpr int KG = C::KG, NS = C::NS, TILE_ELEMS = C::TILE_ELEMS;
-  constexpr int STAGE_ELEMS = C::STAGE_ELEMS, RPI = C::RPI, LPR = C::LPR, LPT = C::LPT;
+  using C = SplitCfg<D, FP8>;
+  constexpr int RB = C::RB, KG = C::KG, NS = C::NS, TILE_BYTES = C::TILE_BYTES;
+  constexpr int STAGE_BYTES = C::STAGE_BYTES, RPI = C::RPI, LPR = C::LPR, LPT = C::LPT;
   constexpr int KS = D / 16;                    // MFMA k-steps of Q.K
   constexpr int DB = D / 32;                    // 32-wide d blocks of O
-  // One array per ring stage, always indexed with compile-time stage numbers:
-  // the compiler can then tell that reading one stage does not depend on the
-  // DMA still writing another, and inserts no wait for it.
-  static_assert(NS == 4 || NS == 5, "ring of four or five stages");
-  __shared__ __attribute__((aligned(16))) uint16_t st0[STAGE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t st1[STAGE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t st2[STAGE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t st3[STAGE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t st4[NS == 5 ? STAGE_ELEMS : 8];
-  uint16_t* const stage_buf[5] = {st0, st1, st2, st3, st4};
+  static_assert(!FP8 || D == 128, "the e4m3 cache is built for head_dim 128");
+  // The ring is one array; a stage is always addressed with a compile-time
+  // stage number.  Tiles arrive by asynchronous DMA whose completion is
+  // tracked with explicit counter waits.
+  __shared__ __attribute__((aligned(16))) char ring[NS * STAGE_BYTES];
+  auto stage = [&](int k) { return ring + k * STAGE_BYTES; };
 
   const int s = blockIdx.x;
   const int g = blockIdx.y / a.nchunks;
@@ -156,19 +182,25 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   const int32_t* trow = a.block_table + size_t(b) * a.maxp;
 
   // ---- prologue, part 1: one memory round trip ---------------------------
-  // Scalar loads: the sequence length and the page ids of the first NS-1
-  // tiles.  Vector loads: the page ids of every tile of the split (lane i:
-  // tile i, clamped only when used) and this lane's query row.  All of them
-  // are waited for before any tile load is issued: a register value still in
-  // flight when the tile loop starts makes the compiler drain the whole
-  // memory queue, tile loads included, at the loop entry.
+  // Scalar loads: the sequence length, the page ids of the first NS-1 tiles
+  // and (e4m3 cache) this KV head's two scales.  Vector loads: the page ids
+  // of every tile of the split (lane i: tile i, clamped only when used) and
+  // this lane's query row.  All of them are waited for before any tile load
+  // is issued: a register value still in flight when the tile loop starts
+  // makes the compiler drain the whole memory queue, tile loads included, at
+  // the loop entry.
   int pg0[NS - 1];
   int L_raw;
+  float k_scale = 1.0f, v_scale = 1.0f;
   {
     const cptr_i32 strow = (cptr_i32)(a.block_table) + size_t(b) * a.maxp;
     L_raw = ((cptr_i32)(a.seq_lens))[b];
 #pragma unroll
     for (int k = 0; k < NS - 1; ++k) pg0[k] = strow[page_index(k)];
+    if constexpr (FP8) {
+      k_scale = ((cptr_f32)(a.k_scale))[g];
+      v_scale = ((cptr_f32)(a.v_scale))[g];
+    }
   }
   static_assert(kMaxSplitTiles <= 64, "one lane per tile of a split");
   const int page_ids = trow[page_index(lane)];   // lane i: this wavefront's page of tile i
@@ -177,13 +209,17 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   const bool row_ok = wave_rows && r < a.rows;
   const int i_row = row_ok ? r / a.G : 0;
   const int gg = row_ok ? r - i_row * a.G : 0;
+  // Q^T operand of k-step ks: 8 values of this lane's query row.  bf16 cache:
+  // d = 16 ks + 8 half + 0..7.  e4m3 cache: d = 32 (ks/2) + 16 half + 8 (ks%2)
+  // + 0..7, matching the 16-byte K reads below (one read feeds two k-steps).
   u32x4 qraw[KS];
   {
-    const uint16_t* qp = a.q + ((size_t(b) * a.K + i_row) * a.Hq + size_t(g) * a.G + gg) * D + half * 8;
+    const uint16_t* qp = a.q + ((size_t(b) * a.K + i_row) * a.Hq + size_t(g) * a.G + gg) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = FP8 ? 32 * (ks >> 1) + 16 * half + 8 * (ks & 1) : 16 * ks + 8 * half;
       qraw[ks] = u32x4{0u, 0u, 0u, 0u};
-      if (row_ok) qraw[ks] = *reinterpret_cast<const u32x4*>(qp + ks * 16);
+      if (row_ok) qraw[ks] = *reinterpret_cast<const u32x4*>(qp + d0);
     }
   }
   // The empty asm takes the scalar results as operands and clobbers memory:
@@ -191,6 +227,7 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   // flight together before the single wait below.
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) asm volatile("" ::"s"(pg0[k]));
+  if constexpr (FP8) asm volatile("" ::"s"(k_scale), "s"(v_scale));
   asm volatile("" ::"s"(L_raw) : "memory");
   __builtin_amdgcn_s_waitcnt(0);                 // vmcnt(0) expcnt(0) lgkmcnt(0)
 
@@ -202,10 +239,10 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
 
   // ---- where this wavefront's share of each tile comes from ---------------
   // Wavefront w fetches tile rows 8w .. 8w+7 (half of page w/2) of K and V.
-  // K rows keep granule c at c ^ (t % KG); V rows keep it at c ^ 2(t % (KG/2))
-  // (granule pairs stay together for the transposing reads).
-  const size_t page_bytes = size_t(a.Hkv) * ORTHRUS_PAGE_SIZE * D * 2;
-  const size_t blk_row = size_t(a.Hkv) * D;
+  // Lane l of a 1 KiB load fills physical granule l % KG of one row, so it
+  // fetches the logical granule that the swizzle puts there.
+  const size_t page_bytes = size_t(a.Hkv) * ORTHRUS_PAGE_SIZE * RB;
+  const size_t blk_row = size_t(a.Hkv) * RB;
   const int lrow = lane / KG;                    // row within one 1 KiB load
   const int lgran = lane % KG;                   // physical granule this lane fills
   uint32_t koff[LPR], voff[LPR];                 // byte offsets inside the half page
@@ -214,25 +251,23 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   for (int j = 0; j < LPR; ++j) {
     const int t = 8 * wave + j * RPI + lrow;     // tile row
     trow_of[j] = t;
-    const int ck = lgran ^ (t & (KG - 1));
-    const int cv = lgran ^ (2 * (t & (KG / 2 - 1)));
-    koff[j] = uint32_t(((t & 15) * D + ck * 8) * 2);
-    voff[j] = uint32_t(((t & 15) * D + cv * 8) * 2);
+    koff[j] = uint32_t((t & 15) * RB + (lgran ^ C::kswz(t)) * 16);
+    voff[j] = uint32_t((t & 15) * RB + (lgran ^ C::vswz(t)) * 16);
   }
-  const char* kpool = reinterpret_cast<const char*>(a.k_pages + size_t(g) * ORTHRUS_PAGE_SIZE * D);
-  const char* vpool = reinterpret_cast<const char*>(a.v_pages + size_t(g) * ORTHRUS_PAGE_SIZE * D);
-  const uint16_t* kblk = a.k_blk + (size_t(b) * a.K * a.Hkv + g) * D;
-  const uint16_t* vblk = a.v_blk + (size_t(b) * a.K * a.Hkv + g) * D;
+  const char* kpool = reinterpret_cast<const char*>(a.k_pages) + size_t(g) * ORTHRUS_PAGE_SIZE * RB;
+  const char* vpool = reinterpret_cast<const char*>(a.v_pages) + size_t(g) * ORTHRUS_PAGE_SIZE * RB;
+  const char* kblk = reinterpret_cast<const char*>(a.k_blk) + (size_t(b) * a.K * a.Hkv + g) * RB;
+  const char* vblk = reinterpret_cast<const char*>(a.v_blk) + (size_t(b) * a.K * a.Hkv + g) * RB;
 
-  auto issue_tile = [&](int ts, int page, uint16_t* sbuf) {
+  auto issue_tile = [&](int ts, int page, char* sbuf) {
     const char* kbase = kpool + size_t(page) * page_bytes;
     const char* vbase = vpool + size_t(page) * page_bytes;
-    uint16_t* dst = sbuf + wave * LPR * 512;
+    char* dst = sbuf + wave * LPR * 1024;
     if (ts + kTile <= L) {                       // uniform: whole tile from the cache
 #pragma unroll
       for (int j = 0; j < LPR; ++j) {
-        load_lds16(kbase + koff[j], lds_addr(dst + j * 512));
-        load_lds16(vbase + voff[j], lds_addr(dst + TILE_ELEMS + j * 512));
+        load_lds16(kbase + koff[j], lds_addr(dst + j * 1024));
+        load_lds16(vbase + voff[j], lds_addr(dst + TILE_BYTES + j * 1024));
       }
     } else {
 #pragma unroll
@@ -241,25 +276,24 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
         const void* ks = kbase + koff[j];
         const void* vs = vbase + voff[j];
         if (p >= L) {
-          const int ck = lgran ^ (trow_of[j] & (KG - 1));
-          const int cv = lgran ^ (2 * (trow_of[j] & (KG / 2 - 1)));
-          ks = p < N ? static_cast<const void*>(kblk + (p - L) * blk_row + ck * 8) : g_zero16;
-          vs = p < N ? static_cast<const void*>(vblk + (p - L) * blk_row + cv * 8) : g_zero16;
+          const int t = trow_of[j];
+          ks = p < N ? static_cast<const void*>(kblk + (p - L) * blk_row + (lgran ^ C::kswz(t)) * 16) : g_zero16;
+          vs = p < N ? static_cast<const void*>(vblk + (p - L) * blk_row + (lgran ^ C::vswz(t)) * 16) : g_zero16;
         }
-        load_lds16(ks, lds_addr(dst + j * 512));
-        load_lds16(vs, lds_addr(dst + TILE_ELEMS + j * 512));
+        load_lds16(ks, lds_addr(dst + j * 1024));
+        load_lds16(vs, lds_addr(dst + TILE_BYTES + j * 1024));
       }
     }
   };
   // A tile past the end of the split: the same number of loads, all from the
   // 16 zero bytes, so that every step of the ring issues the same count and
   // the waits below are fixed numbers.
-  auto issue_dummy = [&](uint16_t* sbuf) {
-    uint16_t* dst = sbuf + wave * LPR * 512;
+  auto issue_dummy = [&](char* sbuf) {
+    char* dst = sbuf + wave * LPR * 1024;
 #pragma unroll
     for (int j = 0; j < LPR; ++j) {
-      load_lds16(g_zero16, lds_addr(dst + j * 512));
-      load_lds16(g_zero16, lds_addr(dst + TILE_ELEMS + j * 512));
+      load_lds16(g_zero16, lds_addr(dst + j * 1024));
+      load_lds16(g_zero16, lds_addr(dst + TILE_BYTES + j * 1024));
     }
   };
   auto clamp_page = [&](int p) { return min(max(p, 0), a.num_pages - 1); };
@@ -267,8 +301,8 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   // ---- prologue, part 2: the first NS-1 tiles -----------------------------
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) {
-    if (k < ntiles) issue_tile(start + k * kTile, clamp_page(pg0[k]), stage_buf[k]);
-    else issue_dummy(stage_buf[k]);
+    if (k < ntiles) issue_tile(start + k * kTile, clamp_page(pg0[k]), stage(k));
+    else issue_dummy(stage(k));
   }
 
   // ---- running softmax state (per lane = per query row, this token half) --
@@ -281,20 +315,40 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   float m_run = -__builtin_inff();
   float l_run = 0.f;
   const int row_limit = VERIFY ? (L + i_row) : (N - 1);  // last visible position
-  const float c = a.scale_log2;
+  // e4m3 cache: a key's value is code * k_scale, so the scale joins the score scale
+  const float c = FP8 ? a.scale_log2 * k_scale : a.scale_log2;
+  // Transposing V reads (A = V^T of the P.V product).  Lane l of the MFMA
+  // operand holds d = l % 32 and the 8 tokens whose probabilities lane l's
+  // P^T operand holds: 16 k2 + 8 (j / 4) + 4 (l / 32) + j % 4, j = 0..7.
   const int trk = lane & 15;
-  const int tr_dofs = 16 * ((lane >> 4) & 1) + 4 * (trk & 3);   // + db*32
-  const int tr_tofs = 4 * half + (trk >> 2);                      // + th*32 + 16*k2 (+8)
+  const int tr_dofs = 16 * ((lane >> 4) & 1) + 4 * (trk & 3);   // bf16 (+ db*32)
+  const int tr_tofs = 4 * half + (trk >> 2);                      // bf16 (+ th*32 + 16*k2, + 8)
+  // e4m3: lane trk of each 16-lane group names one 8-byte piece of the 8x16
+  // byte block the read transposes: row trk/2 (a token), bytes 8 (trk%2)
+  // of d = 16 ((lane/16) % 2) + 32 db .. +15; lane trk receives column trk.
+  const int jr8 = trk >> 1;
+  const int tr8_tok = 8 * (jr8 >> 2) + 4 * half + (jr8 & 3);     // + th*32 + 16*k2
+  const int tr8_gran = (lane >> 4) & 1;                           // + 2*db
+  const int tr8_byte = 8 * (trk & 1);
 
   // Raw scores S^T of one tile for this wavefront: this lane's query row
   // against 16 of the 32 tokens of its half (A = K rows from LDS, B = Q).
-  auto qk = [&](const uint16_t* ks) {
+  auto qk = [&](const char* ks) {
     const int tok = th * 32 + col;
     bf16x8 kf[KS];
+    if constexpr (FP8) {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int gk = kk * 2 + half;
-      kf[kk] = *reinterpret_cast<const bf16x8*>(ks + tok * D + ((gk ^ (tok & (KG - 1))) * 8));
+      for (int m = 0; m < KS / 2; ++m) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(ks + tok * RB + (((2 * m + half) ^ C::kswz(tok)) * 16));
+        kf[2 * m] = e4m3x8_to_bf16(raw[0], raw[1]);
+        kf[2 * m + 1] = e4m3x8_to_bf16(raw[2], raw[3]);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int gk = kk * 2 + half;
+        kf[kk] = *reinterpret_cast<const bf16x8*>(ks + tok * RB + ((gk ^ C::kswz(tok)) * 16));
+      }
     }
     f32x16 acc = f32x16{};
 #pragma unroll
@@ -311,7 +365,7 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   wait_vmcnt<(NS - 2) * LPT>();                                  // tile 0 has landed
   lds_barrier();
   f32x16 sacc = f32x16{};
-  if (wave_rows) sacc = qk(stage_buf[0]);
+  if (wave_rows) sacc = qk(stage(0));
 
   for (int t0 = 0; t0 < ntiles; t0 += NS) {
 #pragma unroll
@@ -352,13 +406,13 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
         lds_barrier();                                             // ... for every wavefront
         if (t - 1 + NS < ntiles)
           issue_tile(ts + (NS - 1) * kTile, clamp_page(__builtin_amdgcn_readlane(page_ids, t - 1 + NS)),
-                     stage_buf[(k + NS - 1) % NS]);
+                     stage((k + NS - 1) % NS));
         else
-          issue_dummy(stage_buf[(k + NS - 1) % NS]);
+          issue_dummy(stage((k + NS - 1) % NS));
       }
       if (wave_rows) {
         // scores of tile t+1 (after the last tile: stale LDS, never used)
-        const f32x16 snext = qk(stage_buf[(k + 1) % NS]);
+        const f32x16 snext = qk(stage((k + 1) % NS));
         float lsum = 0.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -367,22 +421,33 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
           lsum += pv;
         }
         l_run += lsum;
-        const uint16_t* vs = stage_buf[k] + TILE_ELEMS;
+        const char* vs = stage(k) + TILE_BYTES;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
           bf16x8 pb;
 #pragma unroll
           for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(sacc[8 * k2 + j]);
-          const int t1 = th * 32 + 16 * k2 + tr_tofs;        // rows t1 and t1 + 8
-          const int sw = 2 * (t1 & (KG / 2 - 1));             // same for t1 + 8
           bf16x8 vf[DB];
+          if constexpr (FP8) {
+            const int t1 = th * 32 + 16 * k2 + tr8_tok;
+            const int sw = C::vswz(t1);
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int d = db * 32 + tr_dofs;
-            const int off = ((((d >> 3) ^ sw) * 8) + (d & 4));
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lptr_bf16x4)(vs + t1 * D + off));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lptr_bf16x4)(vs + (t1 + 8) * D + off));
-            vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            for (int db = 0; db < DB; ++db) {
+              const int off = t1 * RB + ((2 * db + tr8_gran) ^ sw) * 16 + tr8_byte;
+              const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lptr_i32x2)(vs + off));
+              vf[db] = e4m3x8_to_bf16(uint32_t(raw[0]), uint32_t(raw[1]));
+            }
+          } else {
+            const int t1 = th * 32 + 16 * k2 + tr_tofs;        // rows t1 and t1 + 8
+            const int sw = C::vswz(t1);                         // same for t1 + 8
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const int d = db * 32 + tr_dofs;
+              const int off = (((d >> 3) ^ sw) * 8 + (d & 4)) * 2;
+              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lptr_bf16x4)(vs + t1 * RB + off));
+              const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lptr_bf16x4)(vs + (t1 + 8) * RB + off));
+              vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
           }
 #pragma unroll
           for (int db = 0; db < DB; ++db)
@@ -400,7 +465,9 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   // rows padded by 4 floats: lane col writes row col, and the padding puts
   // consecutive rows on different LDS banks
   constexpr int XS = D + 4;
-  float* xo = reinterpret_cast<float*>(rg == 0 ? st0 : rg == 1 ? st1 : rg == 2 ? st2 : st3);
+  constexpr int XREGION = kRowsPerWave * XS + 2 * kRowsPerWave;   // floats per row group
+  static_assert(4 * XREGION * 4 <= NS * STAGE_BYTES, "the exchange fits in the ring");
+  float* xo = reinterpret_cast<float*>(ring) + rg * XREGION;
   float* xml = xo + kRowsPerWave * XS;
   if (wave_rows && th == 1) {
 #pragma unroll
@@ -424,7 +491,8 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   const float wa = __builtin_amdgcn_exp2f(m_run - M_use);
   const float wb = __builtin_amdgcn_exp2f(m_b - M_use);
   const float l_tot = wa * l_run + wb * l_b;
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  // e4m3 cache: a value is code * v_scale, so the scale multiplies the output
+  const float inv = l_tot > 0.f ? (FP8 ? v_scale : 1.0f) / l_tot : 0.f;
   const size_t part = ((size_t(b) * a.Hkv + g) * a.nchunks + chunk) * a.nsplit + s;
   const size_t prow = part * a.rpc + rg * kRowsPerWave + col;
   uint16_t* po = a.part_o + prow * D;
@@ -578,10 +646,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
   *reinterpret_cast<u32x4*>(a.out + size_t(orow) * D + d0) = packed;
 }
 
-template <int D, bool VERIFY>
+template <int D, bool VERIFY, bool FP8>
 hipError_t launch_split(const AttnArgs& a, hipStream_t stream) {
   dim3 grid(a.nsplit, a.Hkv * a.nchunks, a.B);
-  return launch_kernel(&attn_split_kernel<D, VERIFY>, grid, dim3(512), stream, a);
+  return launch_kernel(&attn_split_kernel<D, VERIFY, FP8>, grid, dim3(512), stream, a);
 }
 
 }  // namespace
@@ -590,13 +658,15 @@ hipError_t launch_attention(const AttnPlan& p, const orthrus_kv& kv, const void*
                             const void* k_blk, const void* v_blk, void* out, float scale,
                             bool verify, void* ws, hipStream_t stream) {
   AttnArgs a;
-  a.k_pages = static_cast<const uint16_t*>(kv.k_pages);
-  a.v_pages = static_cast<const uint16_t*>(kv.v_pages);
+  a.k_pages = kv.k_pages;
+  a.v_pages = kv.v_pages;
   a.block_table = kv.block_table;
   a.seq_lens = kv.seq_lens;
+  a.k_scale = kv.k_scale;
+  a.v_scale = kv.v_scale;
   a.q = static_cast<const uint16_t*>(q);
-  a.k_blk = static_cast<const uint16_t*>(k_blk);
-  a.v_blk = static_cast<const uint16_t*>(v_blk);
+  a.k_blk = k_blk;
+  a.v_blk = v_blk;
   a.part_o = static_cast<uint16_t*>(ws);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_o_bytes);
   a.B = p.B; a.K = p.K; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G;
@@ -606,8 +676,12 @@ hipError_t launch_attention(const AttnPlan& p, const orthrus_kv& kv, const void*
   a.scale_log2 = float(double(scale) * 1.4426950408889634);
 
   hipError_t e;
-  if (p.D == 128) e = verify ? launch_split<128, true>(a, stream) : launch_split<128, false>(a, stream);
-  else e = verify ? launch_split<64, true>(a, stream) : launch_split<64, false>(a, stream);
+  if (kv.kv_dtype == ORTHRUS_KV_FP8_E4M3)   // head_dim 128 (checked on the host)
+    e = verify ? launch_split<128, true, true>(a, stream) : launch_split<128, false, true>(a, stream);
+  else if (p.D == 128)
+    e = verify ? launch_split<128, true, false>(a, stream) : launch_split<128, false, false>(a, stream);
+  else
+    e = verify ? launch_split<64, true, false>(a, stream) : launch_split<64, false, false>(a, stream);
   if (e != hipSuccess) return e;
 
   CombineArgs c;

@@ -10,13 +10,15 @@ namespace {
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int fail(std::string* err, int code, const char* msg) {
   if (err) *err = msg;
   return code;
 }
 
-int check_kv(const orthrus_kv* kv, std::string* err) {
+// need_scales: the call reads values (attention), not only bit patterns (commit).
+int check_kv(const orthrus_kv* kv, bool need_scales, std::string* err) {
   if (!kv) return fail(err, ORTHRUS_ERR_INVALID_ARG, "kv descriptor is null");
   if (!kv->k_pages || !kv->v_pages || !kv->block_table || !kv->seq_lens)
     return fail(err, ORTHRUS_ERR_INVALID_ARG, "kv: null k_pages/v_pages/block_table/seq_lens");
@@ -24,6 +26,14 @@ int check_kv(const orthrus_kv* kv, std::string* err) {
     return fail(err, ORTHRUS_ERR_INVALID_ARG, "kv: page pools must be 16-byte aligned");
   if (kv->page_size != ORTHRUS_PAGE_SIZE)
     return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "kv: page_size must be 16");
+  if (kv->kv_dtype != ORTHRUS_KV_BF16 && kv->kv_dtype != ORTHRUS_KV_FP8_E4M3)
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "kv: kv_dtype must be ORTHRUS_KV_BF16 or ORTHRUS_KV_FP8_E4M3");
+  if (kv->kv_dtype == ORTHRUS_KV_FP8_E4M3) {
+    if (kv->head_dim != 128)
+      return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "kv: an e4m3 cache needs head_dim 128");
+    if (need_scales && (!kv->k_scale || !kv->v_scale || !aligned4(kv->k_scale) || !aligned4(kv->v_scale)))
+      return fail(err, ORTHRUS_ERR_INVALID_ARG, "kv: an e4m3 cache needs 4-byte aligned k_scale and v_scale");
+  }
   if (kv->head_dim != 64 && kv->head_dim != 128)
     return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "kv: head_dim must be 64 or 128");
   if (kv->num_kv_heads < 1 || kv->num_pages < 1 || kv->max_pages_per_seq < 1)
@@ -87,7 +97,7 @@ int check_attention(const orthrus_kv* kv, const void* q, const void* k_blk, cons
                     const void* out, int B, int K, int Hq, float scale, int max_ctx,
                     int split_tokens, const void* ws, size_t ws_bytes, AttnPlan* plan,
                     std::string* err) {
-  int rc = check_kv(kv, err);
+  int rc = check_kv(kv, true, err);
   if (rc) return rc;
   std::string why;
   if (!plan_attention_shape(B, K, Hq, kv->num_kv_heads, kv->head_dim, max_ctx, split_tokens, plan, &why)) {
@@ -204,7 +214,7 @@ int check_lmhead_accept(const void* hidden_states, const void* weight, const int
 int check_commit(const orthrus_kv* kv, int layers, int64_t pool_layer_stride, const void* k_blk,
                  const void* v_blk, int64_t blk_layer_stride, const int32_t* n_emit, int B, int K,
                  const int32_t* seq_lens_out, std::string* err) {
-  int rc = check_kv(kv, err);
+  int rc = check_kv(kv, false, err);
   if (rc) return rc;
   if (layers < 1) return fail(err, ORTHRUS_ERR_INVALID_ARG, "num_layers must be >= 1");
   if (B < 0) return fail(err, ORTHRUS_ERR_INVALID_ARG, "batch must be >= 0");
@@ -213,7 +223,8 @@ int check_commit(const orthrus_kv* kv, int layers, int64_t pool_layer_stride, co
   const int64_t blk_elems = int64_t(B) * K * kv->num_kv_heads * kv->head_dim;
   if (layers > 1 && (pool_layer_stride < pool_elems || blk_layer_stride < blk_elems))
     return fail(err, ORTHRUS_ERR_INVALID_ARG, "layer strides smaller than one layer");
-  if (layers > 1 && ((pool_layer_stride * 2) % 16 || (blk_layer_stride * 2) % 16))
+  const int64_t es = kv_elem_bytes(*kv);
+  if (layers > 1 && ((pool_layer_stride * es) % 16 || (blk_layer_stride * es) % 16))
     return fail(err, ORTHRUS_ERR_INVALID_ARG, "layer strides must keep 16-byte alignment");
   if (B == 0) return ORTHRUS_OK;
   if (!k_blk || !v_blk || !n_emit || !seq_lens_out)
@@ -222,6 +233,20 @@ int check_commit(const orthrus_kv* kv, int layers, int64_t pool_layer_stride, co
     return fail(err, ORTHRUS_ERR_INVALID_ARG, "k_blk/v_blk must be 16-byte aligned");
   if (seq_lens_out == kv->seq_lens)
     return fail(err, ORTHRUS_ERR_INVALID_ARG, "seq_lens_out must not alias kv->seq_lens");
+  return ORTHRUS_OK;
+}
+
+int check_quantize(const void* k, const void* v, const float* k_scale, const float* v_scale, int rows,
+                   int Hkv, int D, const void* k_out, const void* v_out, std::string* err) {
+  if (rows < 0 || Hkv < 1 || D < 16 || D % 16)
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "rows >= 0, num_kv_heads >= 1, head_dim a multiple of 16");
+  if (int64_t(rows) * Hkv * D > (int64_t(1) << 40)) return fail(err, ORTHRUS_ERR_INVALID_ARG, "too many elements");
+  if (rows == 0) return ORTHRUS_OK;
+  if (!k || !v || !k_scale || !v_scale || !k_out || !v_out)
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "null k/v/k_scale/v_scale/k_out/v_out");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out) || !aligned4(k_scale) ||
+      !aligned4(v_scale))
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "k/v/k_out/v_out must be 16-byte aligned, scales 4-byte");
   return ORTHRUS_OK;
 }
 

@@ -84,6 +84,12 @@ int check_commit(const orthrus_kv* kv, int layers, int64_t pool_layer_stride, co
                  const void* v_blk, int64_t blk_layer_stride, const int32_t* n_emit, int B, int K,
                  const int32_t* seq_lens_out, std::string* err);
 
+int check_quantize(const void* k, const void* v, const float* k_scale, const float* v_scale, int rows,
+                   int Hkv, int D, const void* k_out, const void* v_out, std::string* err);
+
+// Bytes per cached element (2 for bf16, 1 for e4m3).
+inline int kv_elem_bytes(const orthrus_kv& kv) { return kv.kv_dtype == ORTHRUS_KV_FP8_E4M3 ? 1 : 2; }
+
 const char* status_string(int status);
 
 }  // namespace orthrus

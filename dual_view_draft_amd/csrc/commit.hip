@@ -7,7 +7,9 @@
 // The verify pass's block K/V rows 0 .. n_emit-1 are copied bit for bit to
 // positions L .. L+n_emit-1 of every layer's paged pool; the draft pass's
 // K/V are never stored.  One workgroup per (block row, sequence, layer); each
-// thread moves one 16-byte granule of one KV head's K or V row.
+// thread moves one 16-byte granule of one KV head's K or V row.  The copy is
+// the same for every element type of the cache (bf16, or e4m3 codes that
+// orthrus_quantize_kv produced for the block).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -21,16 +23,16 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct CommitArgs {
-  uint16_t* k_pages;
-  uint16_t* v_pages;
+  char* k_pages;
+  char* v_pages;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  const uint16_t* k_blk;
-  const uint16_t* v_blk;
+  const char* k_blk;
+  const char* v_blk;
   const int32_t* n_emit;
   int32_t* seq_lens_out;
-  int64_t pool_stride, blk_stride;
-  int B, K, Hkv, D, num_pages, maxp;
+  int64_t pool_stride, blk_stride;   // bytes per layer
+  int B, K, Hkv, RB, num_pages, maxp;   // RB: bytes per head row
 };
 
 __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
@@ -48,16 +50,16 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
   const int page = a.block_table[size_t(b) * a.maxp + pi];
   if (static_cast<unsigned>(page) >= static_cast<unsigned>(a.num_pages)) return;
   const int slot = p & 15;
-  const int G16 = a.D / 8;                 // granules per head row
+  const int G16 = a.RB / 16;               // granules per head row
   const int per_tensor = a.Hkv * G16;
   for (int u = threadIdx.x; u < 2 * per_tensor; u += 256) {
     const bool is_v = u >= per_tensor;
     const int w = is_v ? u - per_tensor : u;
     const int g = w / G16, c = w - g * G16;
-    const uint16_t* src = (is_v ? a.v_blk : a.k_blk) + layer * a.blk_stride +
-                          ((size_t(b) * a.K + r) * a.Hkv + g) * a.D + c * 8;
-    uint16_t* dst = (is_v ? a.v_pages : a.k_pages) + layer * a.pool_stride +
-                    ((size_t(page) * a.Hkv + g) * ORTHRUS_PAGE_SIZE + slot) * a.D + c * 8;
+    const char* src = (is_v ? a.v_blk : a.k_blk) + layer * a.blk_stride +
+                      ((size_t(b) * a.K + r) * a.Hkv + g) * a.RB + c * 16;
+    char* dst = (is_v ? a.v_pages : a.k_pages) + layer * a.pool_stride +
+                ((size_t(page) * a.Hkv + g) * ORTHRUS_PAGE_SIZE + slot) * a.RB + c * 16;
     *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
   }
 }
@@ -69,17 +71,18 @@ hipError_t launch_commit(const orthrus_kv& kv, int layers, int64_t pool_layer_st
                          const int32_t* n_emit, int B, int K, int32_t* seq_lens_out,
                          hipStream_t stream) {
   CommitArgs a;
-  a.k_pages = static_cast<uint16_t*>(kv.k_pages);
-  a.v_pages = static_cast<uint16_t*>(kv.v_pages);
+  const int es = kv_elem_bytes(kv);
+  a.k_pages = static_cast<char*>(kv.k_pages);
+  a.v_pages = static_cast<char*>(kv.v_pages);
   a.block_table = kv.block_table;
   a.seq_lens = kv.seq_lens;
-  a.k_blk = static_cast<const uint16_t*>(k_blk);
-  a.v_blk = static_cast<const uint16_t*>(v_blk);
+  a.k_blk = static_cast<const char*>(k_blk);
+  a.v_blk = static_cast<const char*>(v_blk);
   a.n_emit = n_emit;
   a.seq_lens_out = seq_lens_out;
-  a.pool_stride = pool_layer_stride;
-  a.blk_stride = blk_layer_stride;
-  a.B = B; a.K = K; a.Hkv = kv.num_kv_heads; a.D = kv.head_dim;
+  a.pool_stride = pool_layer_stride * es;
+  a.blk_stride = blk_layer_stride * es;
+  a.B = B; a.K = K; a.Hkv = kv.num_kv_heads; a.RB = kv.head_dim * es;
   a.num_pages = kv.num_pages; a.maxp = kv.max_pages_per_seq;
   return launch_kernel(&commit_kernel, dim3(K, B, layers), dim3(256), stream, a);
 }

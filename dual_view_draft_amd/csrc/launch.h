@@ -48,4 +48,8 @@ hipError_t launch_commit(const orthrus_kv& kv, int layers, int64_t pool_layer_st
                          const int32_t* n_emit, int B, int K, int32_t* seq_lens_out,
                          hipStream_t stream);
 
+// bf16 [rows][Hkv][D] -> e4m3 codes with per-head scales, K and V in one launch.
+hipError_t launch_quantize_kv(const void* k, const void* v, const float* k_scale, const float* v_scale,
+                              int rows, int Hkv, int D, void* k_out, void* v_out, hipStream_t stream);
+
 }  // namespace orthrus

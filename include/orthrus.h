@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define ORTHRUS_ABI_VERSION 1
+#define ORTHRUS_ABI_VERSION 2
 #define ORTHRUS_PAGE_SIZE 16   /* tokens per KV page */
 #define ORTHRUS_MAX_BLOCK 64   /* largest block K */
 
@@ -76,15 +76,31 @@ typedef enum orthrus_status {
     ORTHRUS_ERR_HIP = -5                 /* a HIP runtime call failed (launch error) */
 } orthrus_status;
 
+/* Element type of the cached keys and values (orthrus_kv.kv_dtype). */
+#define ORTHRUS_KV_BF16 0
+#define ORTHRUS_KV_FP8_E4M3 1   /* OCP 8-bit E4M3 codes with per-KV-head fp32 scales */
+
 /*
  * Paged KV cache of ONE layer (the shared cache of both views).
- *  k_pages, v_pages : bf16 [num_pages][num_kv_heads][page_size][head_dim].
- *                     One page of one KV head is a contiguous slab of
- *                     page_size * head_dim values.
+ *  k_pages, v_pages : [num_pages][num_kv_heads][page_size][head_dim] elements
+ *                     of kv_dtype.  One page of one KV head is a contiguous
+ *                     slab of page_size * head_dim elements.
  *  block_table      : int32 [batch][max_pages_per_seq]; position p of sequence
  *                     b lives in page block_table[b][p / 16], slot p % 16.
  *  seq_lens         : int32 [batch]; L_b, the number of cached positions.
- *  page_size must be 16; head_dim 64 or 128.
+ *  kv_dtype         : ORTHRUS_KV_BF16 (bf16 bit patterns) or
+ *                     ORTHRUS_KV_FP8_E4M3 (one byte per element).
+ *  k_scale, v_scale : ORTHRUS_KV_FP8_E4M3 only: fp32 [num_kv_heads], device.
+ *                     The key (value) of KV head h that a code c stands for
+ *                     is e4m3(c) * k_scale[h] (v_scale[h]); finite, > 0.
+ *                     Ignored for bf16 (may be NULL).
+ *  page_size must be 16; head_dim 64 or 128 (bf16) or 128 (e4m3).
+ *
+ * The e4m3 cache is not described by the method's pages: it halves the bytes
+ * the attention streams.  Every key and value the attention reads is in the
+ * cache's format, the block's own rows included (orthrus_quantize_kv), so the
+ * verify pass sees a block key exactly as the cache will hold it and Orthrus
+ * still emits greedy decoding's tokens.
  */
 typedef struct orthrus_kv {
     void* k_pages;
@@ -96,6 +112,9 @@ typedef struct orthrus_kv {
     int32_t num_kv_heads;
     int32_t head_dim;
     int32_t max_pages_per_seq;
+    int32_t kv_dtype;
+    const float* k_scale;
+    const float* v_scale;
 } orthrus_kv;
 
 /* Version of this interface (ORTHRUS_ABI_VERSION). */
@@ -135,7 +154,9 @@ ORTHRUS_API size_t orthrus_attn_workspace_bytes(int batch, int block_k, int num_
  * masked.  The block K/V are read, never written to the cache.
  *
  *  q            : bf16 [batch][block_k][num_q_heads][head_dim]   (post-RoPE)
- *  k_blk, v_blk : bf16 [batch][block_k][num_kv_heads][head_dim]  (post-RoPE)
+ *  k_blk, v_blk : [batch][block_k][num_kv_heads][head_dim] in the cache's
+ *                 element type (post-RoPE; e4m3 codes from orthrus_quantize_kv
+ *                 for an e4m3 cache, read with the cache's scales)
  *  out          : bf16 [batch][block_k][num_q_heads][head_dim]   (written)
  *  scale        : score scale, normally 1/sqrt(head_dim); finite, > 0
  *  max_ctx      : host-known upper bound on every L_b (sizes the grid; no
@@ -148,7 +169,9 @@ ORTHRUS_API size_t orthrus_attn_workspace_bytes(int batch, int block_k, int num_
  * group size of at most 16; head_dim in {64, 128}; page_size 16;
  * max_pages_per_seq * 16 >= max_ctx + block_k; batch >= 0 (0 = no-op).
  * Arithmetic: bf16 MFMA products with fp32 accumulation, fp32 online
- * softmax, bf16 output rounded to nearest even.
+ * softmax, bf16 output rounded to nearest even.  An e4m3 cache's codes are
+ * widened to bf16 exactly; k_scale joins the score scale and v_scale
+ * multiplies the output.
  */
 ORTHRUS_API int orthrus_attn_draft(const orthrus_kv* kv, const void* q, const void* k_blk, const void* v_blk,
                        void* out, int batch, int block_k, int num_q_heads, float scale,
@@ -247,8 +270,9 @@ ORTHRUS_API int orthrus_lmhead_accept(const void* hidden_states, const void* wei
  *
  *  kv                 : layer 0's cache; layer l's pools start
  *                       l * pool_layer_stride elements after kv->k_pages / v_pages
- *  k_blk, v_blk       : bf16 [num_layers][batch][block_k][num_kv_heads][head_dim]
- *                       with layer stride blk_layer_stride elements
+ *  k_blk, v_blk       : [num_layers][batch][block_k][num_kv_heads][head_dim] in
+ *                       the cache's element type, with layer stride
+ *                       blk_layer_stride elements
  *  n_emit             : int32 [batch], each in [1, block_k]
  *  seq_lens_out       : int32 [batch] (written); must not alias kv->seq_lens
  * The block table must already cover positions L_b .. L_b + n_emit[b] - 1.
@@ -257,6 +281,24 @@ ORTHRUS_API int orthrus_commit_kv(const orthrus_kv* kv, int num_layers, int64_t 
                       const void* k_blk, const void* v_blk, int64_t blk_layer_stride,
                       const int32_t* n_emit, int batch, int block_k, int32_t* seq_lens_out,
                       void* stream);
+
+/*
+ * Keys and values of new rows in an e4m3 cache's format: for every element x
+ * of KV head h,
+ *   k_out = e4m3(fp32(x) / k_scale[h]),   v_out = e4m3(fp32(x) / v_scale[h])
+ * with the fp32 division rounded to nearest even, then the nearest e4m3 value
+ * (ties to the even code; magnitudes beyond 448 give +-448; a zero result
+ * keeps x's sign).  The block's rows go through this before both attention
+ * passes and the commit, exactly as a token's K/V are written to and read
+ * back from the cache in plain decoding.
+ *  k, v             : bf16 [rows][num_kv_heads][head_dim], finite
+ *  k_scale, v_scale : fp32 [num_kv_heads], finite, > 0
+ *  k_out, v_out     : uint8 [rows][num_kv_heads][head_dim] (written)
+ * 0 <= rows (0 = no-op); head_dim a multiple of 16.
+ */
+ORTHRUS_API int orthrus_quantize_kv(const void* k, const void* v, const float* k_scale,
+                        const float* v_scale, int rows, int num_kv_heads, int head_dim,
+                        void* k_out, void* v_out, void* stream);
 
 #ifdef __cplusplus
 }

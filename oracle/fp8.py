@@ -15,9 +15,10 @@ bias 7 and three mantissa bits:
 Quantisation of a bf16 value x of KV head h with that head's fp32 scale s_h
 (one scale for K and one for V per head and layer):
   code = round_e4m3(fp32(x) / s_h)
-where the division is IEEE fp32 (rounded to nearest even) and round_e4m3 takes
-the nearest e4m3 value, ties to the even code, and maps magnitudes beyond 448
-to 448 (saturating; the sign of a zero result is kept).  The value the
+where the division is IEEE fp32 (rounded to nearest even; a quotient beyond
+the fp32 range is an infinity) and round_e4m3 takes the nearest e4m3 value,
+ties to the even code, and maps magnitudes beyond 448 to 448 (saturating; the
+sign of a zero result is kept).  The value the
 attention sees is decode(code) * s_h.
 
 Which K/V are quantised: every key and value the attention reads, the cached
@@ -63,11 +64,11 @@ _POS_VALUES = e4m3_decode(_POS_CODES)
 
 
 def e4m3_encode(x) -> np.ndarray:
-    """Finite floats -> nearest e4m3 codes (ties to the even code, saturating
-    to +-448, the sign of zero kept)."""
+    """Floats -> nearest e4m3 codes (ties to the even code, magnitudes beyond
+    448, infinities included, saturating to +-448, the sign of zero kept)."""
     x = np.asarray(x, dtype=np.float64)
-    if not np.all(np.isfinite(x)):
-        raise ValueError("e4m3_encode takes finite values only")
+    if np.any(np.isnan(x)):
+        raise ValueError("e4m3_encode: NaN has no saturating code")
     a = np.minimum(np.abs(x), E4M3_MAX)
     hi = np.searchsorted(_POS_VALUES, a, side="left")         # first value >= a
     hi = np.minimum(hi, len(_POS_VALUES) - 1)

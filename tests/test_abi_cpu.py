@@ -47,7 +47,7 @@ def test_binding_covers_every_export():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.orthrus_abi_version() == 1
+    assert lib.orthrus_abi_version() == 2
     assert lib.orthrus_status_string(-3) == b"ORTHRUS_ERR_WORKSPACE_TOO_SMALL"
     assert lib.orthrus_status_string(0) == b"ORTHRUS_OK"
 
@@ -145,3 +145,42 @@ def test_lmhead_workspace_and_argument_checks(lib):
     assert lib.orthrus_lmhead_accept(P, P, P, 1, 65, 128, 1000, P, P, P, P, P, 1 << 20, None) == -2
     assert lib.orthrus_lmhead_accept(None, None, None, 0, 32, 128, 1000, None, None, None, None, None, 0,
                                      None) == 0
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(kv_dtype=2), -1),                                   # unknown element type
+    (dict(kv_dtype=1, head_dim=64), -2),                      # e4m3 needs head_dim 128
+    (dict(kv_dtype=1, k_scale=0x30000, v_scale=0), -1),       # missing scale
+    (dict(kv_dtype=1, k_scale=0x30002, v_scale=0x30000), -1), # misaligned scale
+])
+def test_attention_checks_the_e4m3_cache_descriptor(lib, change, status):
+    import dual_view_draft_amd.binding as b
+    kv = _kv(b, **change)
+    P = ctypes.c_void_p(0x10000)
+    for fn in (lib.orthrus_attn_draft, lib.orthrus_attn_verify):
+        rc = fn(ctypes.byref(kv), P, P, P, P, 1, 32, 32, 0.088, 1000, 0, P, 1 << 40, None)
+        assert rc == status, lib.orthrus_last_error()
+
+
+def test_commit_of_an_e4m3_cache_needs_no_scales(lib):
+    import dual_view_draft_amd.binding as b
+    kv = _kv(b, kv_dtype=1)
+    P = ctypes.c_void_p(0x10000)
+    # a bad layer stride is the first failure, so the scales were not asked for
+    assert lib.orthrus_commit_kv(ctypes.byref(kv), 2, 8, P, P, 0, P, 1, 32, P, None) == -1
+    assert b"stride" in lib.orthrus_last_error()
+    pool = 4096 * 8 * 16 * 128
+    # strides in elements: a 1-byte element needs a multiple of 16 elements
+    assert lib.orthrus_commit_kv(ctypes.byref(kv), 2, pool + 8, P, P, 32 * 8 * 128, P, 1, 32, P, None) == -1
+    assert b"alignment" in lib.orthrus_last_error()
+
+
+def test_quantize_argument_checks(lib):
+    P = ctypes.c_void_p(0x10000)
+    S = ctypes.c_void_p(0x20004)
+    assert lib.orthrus_quantize_kv(None, None, None, None, 0, 8, 128, None, None, None) == 0
+    assert lib.orthrus_quantize_kv(P, P, S, S, 32, 8, 120, P, P, None) == -1     # head_dim % 16
+    assert lib.orthrus_quantize_kv(P, P, S, S, -1, 8, 128, P, P, None) == -1
+    assert lib.orthrus_quantize_kv(P, P, None, S, 32, 8, 128, P, P, None) == -1
+    assert lib.orthrus_quantize_kv(P, P, ctypes.c_void_p(0x20002), S, 32, 8, 128, P, P, None) == -1
+    assert lib.orthrus_quantize_kv(P, ctypes.c_void_p(0x10008), S, S, 32, 8, 128, P, P, None) == -1

@@ -70,8 +70,12 @@ def test_saturation_and_signed_zero():
     assert list(e4m3_encode([448.0, 463.9, 464.0, 480.0, 1e30])) == [0x7E] * 5
     assert list(e4m3_encode([-448.0, -1e30])) == [0xFE, 0xFE]
     assert list(e4m3_encode([0.0, -0.0, 2.0 ** -11, -2.0 ** -11])) == [0x00, 0x80, 0x00, 0x80]
+    assert list(e4m3_encode([np.inf, -np.inf])) == [0x7E, 0xFE]
     with pytest.raises(ValueError):
-        e4m3_encode([np.inf])
+        e4m3_encode([np.nan])
+    # an fp32 quotient that overflows is an infinity and saturates
+    big = f32_to_bf16_bits(np.array([[3.0e38, -3.0e38]], np.float32)).reshape(1, 2, 1)
+    assert list(quantize_kv(big, np.array([1e-5], np.float32)).ravel()) == [0x7E, 0xFE]
 
 
 def test_quantisation_divides_by_the_scale_of_each_head():
