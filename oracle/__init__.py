@@ -21,6 +21,8 @@ Modules:
   consensus  - vocabulary argmax, longest-prefix acceptance, cache commit
   lmhead     - LM-head projection of the final hidden states and the greedy
                token of every row
+  sampling   - consensus at temperature > 0 (speculative sampling, a stated
+               reading; the pages give only the greedy rule)
   fp8        - an e4m3 KV cache: the format, quantisation with per-head
                scales, and attention over the decoded values (a stated
                reading; the pages describe no quantised cache)
