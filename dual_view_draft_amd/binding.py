@@ -69,6 +69,13 @@ EXPORTS = {
                                          ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_void_p, ctypes.c_void_p]),
     "orthrus_quantize_kv": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3),
+    "orthrus_sample_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 2),
+    "orthrus_sample": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p]),
+    "orthrus_accept_sampled_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 3),
+    "orthrus_accept_sampled": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_float] +
+                               [ctypes.c_void_p] * 6 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
 }
 EXPORTS["orthrus_attn_verify"] = EXPORTS["orthrus_attn_draft"]
 
@@ -343,3 +350,55 @@ def orthrus_quantize_kv(k: torch.Tensor, v: torch.Tensor, k_scale: torch.Tensor,
     rc = load_library().orthrus_quantize_kv(_ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), rows, Hkv, D,
                                             _ptr(k_out), _ptr(v_out), _stream(stream))
     _check(rc, "orthrus_quantize_kv")
+
+
+def orthrus_sample_workspace_bytes(rows: int, vocab: int) -> int:
+    return load_library().orthrus_sample_workspace_bytes(rows, vocab)
+
+
+def orthrus_sample(logits: torch.Tensor, temperature: float, u: torch.Tensor, out: torch.Tensor, *,
+                   workspace=None, stream=None):
+    """out[r] = inverse-CDF draw of softmax(logits[r] / temperature) with uniform u[r]
+    (logits fp32 [..., V]; u fp32 and out int32 with one entry per row)."""
+    if logits.dtype != torch.float32 or u.dtype != torch.float32 or out.dtype != torch.int32:
+        raise ValueError("logits and u must be float32, out int32")
+    V = logits.shape[-1]
+    rows = logits.numel() // V
+    if u.numel() != rows or out.numel() != rows:
+        raise ValueError("one uniform and one output per row")
+    if workspace is None:
+        workspace = torch.empty(orthrus_sample_workspace_bytes(rows, V), dtype=torch.uint8, device=logits.device)
+    rc = load_library().orthrus_sample(_ptr(logits), rows, V, float(temperature), _ptr(u), _ptr(out),
+                                       _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "orthrus_sample")
+    return out
+
+
+def orthrus_accept_sampled_workspace_bytes(batch: int, block_k: int, vocab: int) -> int:
+    return load_library().orthrus_accept_sampled_workspace_bytes(batch, block_k, vocab)
+
+
+def orthrus_accept_sampled(logits_d: torch.Tensor, logits_a: torch.Tensor, draft: torch.Tensor,
+                           temperature: float, u_acc: torch.Tensor, u_res: torch.Tensor, tokens, n_acc, n_emit,
+                           next_anchor, *, workspace=None, stream=None):
+    """Speculative-sampling consensus of the draft and AR views' logits [B, K, V] (fp32)."""
+    if logits_d.dtype != torch.float32 or logits_a.dtype != torch.float32:
+        raise ValueError("logits must be float32")
+    if u_acc.dtype != torch.float32 or u_res.dtype != torch.float32:
+        raise ValueError("uniforms must be float32")
+    for t in (draft, tokens, n_acc, n_emit, next_anchor):
+        if t.dtype != torch.int32:
+            raise ValueError("token and count tensors must be int32")
+    B, K, V = logits_a.shape
+    if tuple(logits_d.shape) != (B, K, V):
+        raise ValueError("logits_d and logits_a shapes differ")
+    if workspace is None:
+        n = orthrus_accept_sampled_workspace_bytes(B, K, V)
+        if n == 0:
+            raise ValueError("unsupported consensus shape")
+        workspace = torch.empty(n, dtype=torch.uint8, device=logits_a.device)
+    rc = load_library().orthrus_accept_sampled(_ptr(logits_d), _ptr(logits_a), _ptr(draft), B, K, V,
+                                               float(temperature), _ptr(u_acc), _ptr(u_res), _ptr(tokens),
+                                               _ptr(n_acc), _ptr(n_emit), _ptr(next_anchor), _ptr(workspace),
+                                               workspace.numel(), _stream(stream))
+    _check(rc, "orthrus_accept_sampled")

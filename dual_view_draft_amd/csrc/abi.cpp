@@ -188,6 +188,54 @@ int orthrus_commit_kv(const orthrus_kv* kv, int num_layers, int64_t pool_layer_s
   }
 }
 
+size_t orthrus_sample_workspace_bytes(int rows, int vocab) {
+  orthrus::SamplePlan plan;
+  if (!orthrus::plan_sample(rows, 0, vocab, &plan)) return 0;
+  return plan.ws_bytes;
+}
+
+int orthrus_sample(const float* logits, int rows, int vocab, float temperature, const float* u, int32_t* out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    orthrus::SamplePlan plan;
+    std::string err;
+    const int rc = orthrus::check_sample(logits, rows, vocab, temperature, u, out, workspace, workspace_bytes,
+                                         &plan, &err);
+    if (rc != ORTHRUS_OK) return fail(rc, err);
+    if (rows == 0) return ORTHRUS_OK;
+    return hip_status(orthrus::launch_sample(plan, logits, temperature, u, out, workspace, as_stream(stream)));
+  } catch (...) {
+    return fail(ORTHRUS_ERR_HIP, "internal error");
+  }
+}
+
+size_t orthrus_accept_sampled_workspace_bytes(int batch, int block_k, int vocab) {
+  orthrus::SamplePlan plan;
+  if (batch < 0 || block_k < 1 || int64_t(batch) * block_k * 2 > 65535) return 0;
+  if (!orthrus::plan_sample(2 * batch * block_k, batch, vocab, &plan)) return 0;
+  return plan.ws_bytes;
+}
+
+int orthrus_accept_sampled(const float* logits_d, const float* logits_a, const int32_t* draft, int batch,
+                           int block_k, int vocab, float temperature, const float* u_acc, const float* u_res,
+                           int32_t* tokens, int32_t* n_acc, int32_t* n_emit, int32_t* next_anchor,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    orthrus::SamplePlan plan;
+    std::string err;
+    const int rc = orthrus::check_accept_sampled(logits_d, logits_a, draft, batch, block_k, vocab, temperature,
+                                                 u_acc, u_res, tokens, n_acc, n_emit, next_anchor, workspace,
+                                                 workspace_bytes, &plan, &err);
+    if (rc != ORTHRUS_OK) return fail(rc, err);
+    if (batch == 0) return ORTHRUS_OK;
+    return hip_status(orthrus::launch_accept_sampled(plan, logits_d, logits_a, draft, batch, block_k,
+                                                     temperature, u_acc, u_res, tokens, n_acc, n_emit,
+                                                     next_anchor, workspace, as_stream(stream)));
+  } catch (...) {
+    return fail(ORTHRUS_ERR_HIP, "internal error");
+  }
+}
+
 int orthrus_quantize_kv(const void* k, const void* v, const float* k_scale, const float* v_scale, int rows,
                         int num_kv_heads, int head_dim, void* k_out, void* v_out, void* stream) {
   try {

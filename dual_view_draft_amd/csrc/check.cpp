@@ -236,6 +236,64 @@ int check_commit(const orthrus_kv* kv, int layers, int64_t pool_layer_stride, co
   return ORTHRUS_OK;
 }
 
+bool plan_sample(int stat_rows, int B, int V, SamplePlan* p) {
+  if (stat_rows < 0 || B < 0 || V < 1) return false;
+  p->rows = stat_rows;
+  p->B = B;
+  p->V = V;
+  // about 2048 workgroups over the statistics, 4096..16384 values per chunk
+  int64_t chunk = round_up(ceil_div(int64_t(V) * (stat_rows > 0 ? stat_rows : 1), 2048), 1024);
+  if (chunk < 4096) chunk = 4096;
+  if (chunk > 16384) chunk = 16384;
+  if (chunk > V) chunk = V;
+  p->chunk = int(chunk);
+  p->nchunks = int(ceil_div(V, chunk));
+  const int64_t cells = int64_t(stat_rows > 0 ? stat_rows : 1) * p->nchunks;
+  p->cm_off = 0;
+  p->cs_off = size_t(round_up(cells * 4, 256));
+  p->seq_off = p->cs_off + size_t(round_up(cells * 8, 256));
+  p->rs_off = p->seq_off + size_t(round_up(int64_t(B > 0 ? B : 1) * kSampleSeqBytes, 256));
+  p->ws_bytes = p->rs_off + size_t(round_up(int64_t(B > 0 ? B : 1) * p->nchunks * 8, 256));
+  return true;
+}
+
+int check_sample(const float* logits, int rows, int V, float temperature, const float* u, const int32_t* out,
+                 const void* ws, size_t ws_bytes, SamplePlan* plan, std::string* err) {
+  if (rows < 0 || V < 1) return fail(err, ORTHRUS_ERR_INVALID_ARG, "rows must be >= 0 and vocab >= 1");
+  if (rows > 65535) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "at most 65535 rows per call");
+  if (!(std::isfinite(temperature) && temperature > 0.f))
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "temperature must be finite and > 0");
+  plan_sample(rows, 0, V, plan);
+  if (rows == 0) return ORTHRUS_OK;
+  if (!logits || !u || !out) return fail(err, ORTHRUS_ERR_INVALID_ARG, "null logits/u/out");
+  if (!ws || !aligned16(ws)) return fail(err, ORTHRUS_ERR_INVALID_ARG, "workspace null or misaligned");
+  if (ws_bytes < plan->ws_bytes)
+    return fail(err, ORTHRUS_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than orthrus_sample_workspace_bytes()");
+  return ORTHRUS_OK;
+}
+
+int check_accept_sampled(const float* logits_d, const float* logits_a, const int32_t* draft, int B, int K,
+                         int V, float temperature, const float* u_acc, const float* u_res,
+                         const int32_t* tokens, const int32_t* n_acc, const int32_t* n_emit,
+                         const int32_t* next_anchor, const void* ws, size_t ws_bytes, SamplePlan* plan,
+                         std::string* err) {
+  if (B < 0) return fail(err, ORTHRUS_ERR_INVALID_ARG, "batch must be >= 0");
+  if (K < 1 || K > ORTHRUS_MAX_BLOCK) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "block_k must be in [1, 64]");
+  if (V < 1) return fail(err, ORTHRUS_ERR_INVALID_ARG, "vocab must be >= 1");
+  if (int64_t(B) * K * 2 > 65535) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "2 * batch * block_k must be <= 65535");
+  if (!(std::isfinite(temperature) && temperature > 0.f))
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "temperature must be finite and > 0");
+  plan_sample(2 * B * K, B, V, plan);
+  if (B == 0) return ORTHRUS_OK;
+  if (!logits_d || !logits_a || !draft || !u_acc || !u_res || !tokens || !n_acc || !n_emit || !next_anchor)
+    return fail(err, ORTHRUS_ERR_INVALID_ARG, "null pointer argument");
+  if (!ws || !aligned16(ws)) return fail(err, ORTHRUS_ERR_INVALID_ARG, "workspace null or misaligned");
+  if (ws_bytes < plan->ws_bytes)
+    return fail(err, ORTHRUS_ERR_WORKSPACE_TOO_SMALL,
+                "workspace smaller than orthrus_accept_sampled_workspace_bytes()");
+  return ORTHRUS_OK;
+}
+
 int check_quantize(const void* k, const void* v, const float* k_scale, const float* v_scale, int rows,
                    int Hkv, int D, const void* k_out, const void* v_out, std::string* err) {
   if (rows < 0 || Hkv < 1 || D < 16 || D % 16)

@@ -84,6 +84,29 @@ int check_commit(const orthrus_kv* kv, int layers, int64_t pool_layer_stride, co
                  const void* v_blk, int64_t blk_layer_stride, const int32_t* n_emit, int B, int K,
                  const int32_t* seq_lens_out, std::string* err);
 
+// Temperature sampling and the speculative-sampling consensus: vocabulary
+// chunks of every row with statistics (m fp32, s fp64 per chunk), the
+// per-sequence acceptance state and the residual chunk sums.
+constexpr int kSampleSeqBytes = 32;
+
+struct SamplePlan {
+  int rows = 0;          // rows with chunk statistics
+  int B = 0, V = 0, chunk = 0, nchunks = 0;
+  size_t cm_off = 0, cs_off = 0, seq_off = 0, rs_off = 0, ws_bytes = 0;
+};
+
+// stat_rows: rows of orthrus_sample, or 2*B*K for the consensus (B sequences).
+bool plan_sample(int stat_rows, int B, int V, SamplePlan* plan);
+
+int check_sample(const float* logits, int rows, int V, float temperature, const float* u, const int32_t* out,
+                 const void* ws, size_t ws_bytes, SamplePlan* plan, std::string* err);
+
+int check_accept_sampled(const float* logits_d, const float* logits_a, const int32_t* draft, int B, int K,
+                         int V, float temperature, const float* u_acc, const float* u_res,
+                         const int32_t* tokens, const int32_t* n_acc, const int32_t* n_emit,
+                         const int32_t* next_anchor, const void* ws, size_t ws_bytes, SamplePlan* plan,
+                         std::string* err);
+
 int check_quantize(const void* k, const void* v, const float* k_scale, const float* v_scale, int rows,
                    int Hkv, int D, const void* k_out, const void* v_out, std::string* err);
 

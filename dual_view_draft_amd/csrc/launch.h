@@ -48,6 +48,15 @@ hipError_t launch_commit(const orthrus_kv& kv, int layers, int64_t pool_layer_st
                          const int32_t* n_emit, int B, int K, int32_t* seq_lens_out,
                          hipStream_t stream);
 
+// Temperature sampling (statistics + one draw per row) and the
+// speculative-sampling consensus (statistics, acceptance, residual draw).
+hipError_t launch_sample(const SamplePlan& plan, const float* logits, float temperature, const float* u,
+                         int32_t* out, void* ws, hipStream_t stream);
+hipError_t launch_accept_sampled(const SamplePlan& plan, const float* logits_d, const float* logits_a,
+                                 const int32_t* draft, int B, int K, float temperature, const float* u_acc,
+                                 const float* u_res, int32_t* tokens, int32_t* n_acc, int32_t* n_emit,
+                                 int32_t* next_anchor, void* ws, hipStream_t stream);
+
 // bf16 [rows][Hkv][D] -> e4m3 codes with per-head scales, K and V in one launch.
 hipError_t launch_quantize_kv(const void* k, const void* v, const float* k_scale, const float* v_scale,
                               int rows, int Hkv, int D, void* k_out, void* v_out, hipStream_t stream);

@@ -283,6 +283,57 @@ ORTHRUS_API int orthrus_commit_kv(const orthrus_kv* kv, int num_layers, int64_t 
                       void* stream);
 
 /*
+ * Consensus at temperature T > 0.  The pages give the acceptance rule for
+ * greedy decoding only (section 2.3 step 3) and state that the output
+ * distribution is the AR model's (Hacker News thread, post #21); for T > 0
+ * this library takes the standard speculative-sampling rule.  Every random
+ * choice is an inverse-CDF draw with a caller-supplied uniform u in [0, 1):
+ * the smallest token v whose cumulative weight exceeds u times the total
+ * weight.  Probabilities, exponentials and cumulative weights are evaluated
+ * in fp64 from the fp32 logits, so a draw agrees with an exact evaluation
+ * except when u lies within about 1e-15 (relative) of a threshold.
+ */
+
+/* Bytes of device workspace for orthrus_sample (0 if invalid). */
+ORTHRUS_API size_t orthrus_sample_workspace_bytes(int rows, int vocab);
+
+/*
+ * Temperature sampling (the drafted tokens at T > 0): out[r] = draw of
+ * softmax(logits[r] / temperature) with uniform u[r].
+ *  logits : fp32 [rows][vocab], finite
+ *  u      : fp32 [rows], each in [0, 1)
+ *  out    : int32 [rows] (written)
+ * 0 <= rows <= 65535 (0 = no-op); temperature finite and > 0.
+ */
+ORTHRUS_API int orthrus_sample(const float* logits, int rows, int vocab, float temperature, const float* u,
+                   int32_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace for orthrus_accept_sampled (0 if invalid). */
+ORTHRUS_API size_t orthrus_accept_sampled_workspace_bytes(int batch, int block_k, int vocab);
+
+/*
+ * Speculative-sampling consensus.  With q_i = softmax(logits_d[b][i] / T)
+ * (draft view) and p_i = softmax(logits_a[b][i] / T) (AR view, the verify
+ * pass), left to right: drafted token d_i is accepted when
+ * u_acc[b][i] * q_i(d_i) < p_i(d_i); at the first row j that fails, the
+ * emitted token is a draw of max(0, p_j - q_j) (normalised) with u_res[b][j]
+ * and the step ends.  If every row passes, the K drafted tokens are emitted.
+ * The emitted tokens follow the AR view's distribution whatever q is; as
+ * T -> 0 this is orthrus_accept's greedy rule.
+ *  logits_d, logits_a : fp32 [batch][block_k][vocab], finite
+ *  draft              : int32 [batch][block_k], the drafted tokens
+ *  u_acc, u_res       : fp32 [batch][block_k], each in [0, 1)
+ *  tokens             : int32 [batch][block_k] (written) emitted tokens in
+ *                       [0, n_emit), -1 after
+ *  n_acc, n_emit, next_anchor : int32 [batch] (written), as in orthrus_accept
+ * 1 <= block_k <= 64; 2 * batch * block_k <= 65535; temperature finite, > 0.
+ */
+ORTHRUS_API int orthrus_accept_sampled(const float* logits_d, const float* logits_a, const int32_t* draft,
+                           int batch, int block_k, int vocab, float temperature, const float* u_acc,
+                           const float* u_res, int32_t* tokens, int32_t* n_acc, int32_t* n_emit,
+                           int32_t* next_anchor, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Keys and values of new rows in an e4m3 cache's format: for every element x
  * of KV head h,
  *   k_out = e4m3(fp32(x) / k_scale[h]),   v_out = e4m3(fp32(x) / v_scale[h])

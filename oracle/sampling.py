@@ -97,7 +97,10 @@ def speculative_accept(logits_d, logits_a, d, T: float, u_acc, u_res):
             if float(u_acc[b, i]) * q[t] < p[t]:
                 tokens[b, i] = t
                 continue
-            tokens[b, i] = inverse_cdf(np.maximum(p - q, 0.0), float(u_res[b, i]))
+            r = np.maximum(p - q, 0.0)
+            if not r.sum() > 0:          # p == q: a rejection cannot happen; kept total
+                r = p
+            tokens[b, i] = inverse_cdf(r, float(u_res[b, i]))
             j = i
             break
         n_acc[b] = j

@@ -184,3 +184,26 @@ def test_quantize_argument_checks(lib):
     assert lib.orthrus_quantize_kv(P, P, None, S, 32, 8, 128, P, P, None) == -1
     assert lib.orthrus_quantize_kv(P, P, ctypes.c_void_p(0x20002), S, 32, 8, 128, P, P, None) == -1
     assert lib.orthrus_quantize_kv(P, ctypes.c_void_p(0x10008), S, S, 32, 8, 128, P, P, None) == -1
+
+
+def test_sampling_workspace_and_argument_checks(lib):
+    P = ctypes.c_void_p(0x10000)
+    n = lib.orthrus_sample_workspace_bytes(32, 151936)
+    assert n >= 32 * 12 * (4 + 8)                       # chunk statistics of every row
+    assert lib.orthrus_sample_workspace_bytes(-1, 10) == 0
+    assert lib.orthrus_sample(None, 0, 151936, ctypes.c_float(1.0), None, None, None, 0, None) == 0
+    assert lib.orthrus_sample(P, 4, 1000, ctypes.c_float(0.0), P, P, P, 1 << 20, None) == -1
+    assert lib.orthrus_sample(P, 4, 1000, ctypes.c_float(float("inf")), P, P, P, 1 << 20, None) == -1
+    assert lib.orthrus_sample(P, 4, 1000, ctypes.c_float(1.0), None, P, P, 1 << 20, None) == -1
+    assert lib.orthrus_sample(P, 4, 1000, ctypes.c_float(1.0), P, P, P, 8, None) == -3
+    m = lib.orthrus_accept_sampled_workspace_bytes(4, 32, 151936)
+    assert m > lib.orthrus_sample_workspace_bytes(2 * 4 * 32, 151936)   # plus the per-sequence state
+    assert lib.orthrus_accept_sampled_workspace_bytes(1024, 64, 1000) == 0   # 2*B*K > 65535
+    F = ctypes.c_float(1.0)
+    assert lib.orthrus_accept_sampled(P, P, P, 1, 65, 1000, F, P, P, P, P, P, P, P, 1 << 20, None) == -2
+    assert lib.orthrus_accept_sampled(P, P, P, 1, 32, 1000, ctypes.c_float(-1.0), P, P, P, P, P, P, P,
+                                      1 << 20, None) == -1
+    assert lib.orthrus_accept_sampled(P, P, P, 1, 32, 1000, F, P, None, P, P, P, P, P, 1 << 20, None) == -1
+    assert lib.orthrus_accept_sampled(P, P, P, 1, 32, 1000, F, P, P, P, P, P, P, P, 64, None) == -3
+    assert lib.orthrus_accept_sampled(None, None, None, 0, 32, 1000, F, None, None, None, None, None, None,
+                                      None, 0, None) == 0
