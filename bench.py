@@ -238,6 +238,47 @@ def main():
                                                                        stream=None)
         op_calls["lmhead_accept"] = lambda i: dv.orthrus_lmhead_accept(lm_h, lm_w, d_tok, a_tok, n_acc, n_emit,
                                                                        nxt, workspace=ws_lm, stream=None)
+    # the same attention over an e4m3 copy of every pool (one scale for all
+    # heads, so the pages can be quantised in their own layout); the block's
+    # rows are quantised with the same scales, as the model does each layer
+    if not args.quick:
+        scale = torch.full((Hkv,), 4.0 / math.sqrt(D) / 448.0, dtype=torch.float32, device=dev)
+
+        def fp8_rows(k, v):
+            ko = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+            vo = torch.empty_like(ko)
+            dv.orthrus_quantize_kv(k, v, scale, scale, ko, vo)
+            return ko, vo
+
+        kvs8 = []
+        for kv in kvs:
+            n = kv.k_pages.shape[0]
+            k8, v8 = fp8_rows(kv.k_pages.view(n * 16, Hkv, D), kv.v_pages.view(n * 16, Hkv, D))
+            kvs8.append(dv.PagedKV(k8.view(kv.k_pages.shape), v8.view(kv.v_pages.shape), kv.block_table,
+                                   kv.seq_lens, k_scale=scale, v_scale=scale))
+        kb8_d, vb8_d = fp8_rows(kb_d, vb_d)
+        kb8_v, vb8_v = fp8_rows(kb_v, vb_v)
+        op_calls["draft_attn_fp8"] = lambda i: dv.orthrus_attn_draft(
+            kvs8[(2 * i) % n_pools], q_d, kb8_d, vb8_d, out_d, max_ctx=max_ctx, split_tokens=args.split,
+            workspace=ws_attn, stream=None)
+        op_calls["verify_attn_fp8"] = lambda i: dv.orthrus_attn_verify(
+            kvs8[(2 * i + 1) % n_pools], q_v, kb8_v, vb8_v, out_v, max_ctx=max_ctx, split_tokens=args.split,
+            workspace=ws_attn, stream=None)
+        # consensus at temperature 1: drafted tokens drawn from the draft
+        # logits, speculative-sampling acceptance against the AR logits
+        gen_u = torch.Generator(device=dev).manual_seed(w["seed"] + 11)
+        u_draft, u_acc, u_res = (torch.rand((B, K), generator=gen_u, device=dev) for _ in range(3))
+        tok_s = torch.empty((B, K), dtype=torch.int32, device=dev)
+        ws_samp = torch.empty(dv.orthrus_sample_workspace_bytes(B * K, V), dtype=torch.uint8, device=dev)
+        ws_accs = torch.empty(dv.orthrus_accept_sampled_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+        op_calls["draft_sample_t1"] = lambda i: dv.orthrus_sample(logits_d, 1.0, u_draft, d_tok, workspace=ws_samp,
+                                                                  stream=None)
+        op_calls["accept_sampled_t1"] = lambda i: dv.orthrus_accept_sampled(
+            logits_d, logits_a, d_tok, 1.0, u_acc, u_res, tok_s, n_acc, n_emit, nxt, workspace=ws_accs,
+            stream=None)
+        op_calls["quantize_block_kv"] = lambda i: dv.orthrus_quantize_kv(kb_v, vb_v, scale, scale, kb8_v, vb8_v,
+                                                                         stream=None)
+        torch.cuda.synchronize()
     op_ms, op_min = {}, {}
     for op, call in ([] if args.quick else op_calls.items()):
         graph = capture(lambda call=call: [call(i) for i in range(REPS)])
@@ -314,6 +355,29 @@ def main():
                      "achieved": round(lm_bytes / lm_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(lm_bytes / lm_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": lm_bytes},
+    }
+    attn8 = ("draft_attn_fp8", "verify_attn_fp8")
+    dom8 = max(attn8, key=lambda o: op_ms[o])
+    attn_bytes8 = (kv_bytes // 2 + 2 * B * K * Hq * D * 2 + 2 * B * K * Hkv * D + 4 * pages_read + 4 * B
+                   + 2 * 4 * Hkv)
+    res["fp8_kv"] = {
+        "kv_dtype": "e4m3 (per-KV-head fp32 scales), attention arithmetic as the bf16 cache's",
+        "op_ms": {o: round(op_ms[o], 4) for o in attn8 + ("quantize_block_kv",)},
+        "attn_kv_gbps": {o: round(kv_bytes / 2 / (op_ms[o] * 1e-3) / 1e9, 1) for o in attn8},
+        "speedup_vs_bf16_cache": {o: round(op_ms[o.replace("_fp8", "")] / op_ms[o], 3) for o in attn8},
+        "roofline": {"kernel": f"{dom8}: attn_split_kernel<e4m3> + attn_combine_kernel (one ABI call)",
+                     "bound": "hbm", "achieved": round(attn_bytes8 / (op_ms[dom8] * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(attn_bytes8 / (op_ms[dom8] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": attn_bytes8,
+                     "mfma_tflops": round(attn_flops / (op_ms[dom8] * 1e-3) / 1e12, 1)},
+    }
+    logit_bytes = B * K * V * 4
+    res["sampling_t1"] = {
+        "op_ms": {o: round(op_ms[o], 4) for o in ("draft_sample_t1", "accept_sampled_t1")},
+        "logits_gbps": {"draft_sample_t1": round(logit_bytes / (op_ms["draft_sample_t1"] * 1e-3) / 1e9, 1),
+                        "accept_sampled_t1": round(2 * logit_bytes / (op_ms["accept_sampled_t1"] * 1e-3) / 1e9, 1)},
+        "note": "fp32 logits read once per statistics pass; fp64 exponentials",
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, case, (qv, kbv, vbv), cons, kv_bytes)
