@@ -248,12 +248,17 @@ bool plan_sample(int stat_rows, int B, int V, SamplePlan* p) {
   if (chunk > V) chunk = V;
   p->chunk = int(chunk);
   p->nchunks = int(ceil_div(V, chunk));
-  const int64_t cells = int64_t(stat_rows > 0 ? stat_rows : 1) * p->nchunks;
+  p->rchunk = kResidualChunk;
+  p->rchunks = B > 0 ? int(ceil_div(V, kResidualChunk)) : 0;
+  const int64_t rows1 = stat_rows > 0 ? stat_rows : 1;
+  const int64_t cells = rows1 * p->nchunks;
   p->cm_off = 0;
   p->cs_off = size_t(round_up(cells * 4, 256));
-  p->seq_off = p->cs_off + size_t(round_up(cells * 8, 256));
+  p->cw_off = p->cs_off + size_t(round_up(cells * 8, 256));
+  p->rn_off = p->cw_off + size_t(round_up(cells * 8, 256));
+  p->seq_off = p->rn_off + size_t(round_up(rows1 * kSampleRowBytes, 256));
   p->rs_off = p->seq_off + size_t(round_up(int64_t(B > 0 ? B : 1) * kSampleSeqBytes, 256));
-  p->ws_bytes = p->rs_off + size_t(round_up(int64_t(B > 0 ? B : 1) * p->nchunks * 8, 256));
+  p->ws_bytes = p->rs_off + size_t(round_up(int64_t(B > 0 ? B : 1) * (p->rchunks > 0 ? p->rchunks : 1) * 8, 256));
   return true;
 }
 

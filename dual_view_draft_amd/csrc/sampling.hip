@@ -15,9 +15,12 @@
 //
 // Work layout.  Rows are cut into vocabulary chunks; a statistics pass
 // writes, per (row, chunk), the chunk's maximum logit m_c (fp32) and
-// s_c = sum exp((z - m_c) / T) (fp64).  A row's maximum M and normaliser
-// Z = sum_c s_c exp((m_c - M) / T) are then combined in chunk order.  A draw
-// finds its chunk from the chunk sums in order and scans that chunk only.
+// s_c = sum exp((z - m_c) / T) (fp64); a wavefront per row then forms the
+// row maximum M, the chunk weights s_c exp((m_c - M) / T) and their sum Z in
+// a fixed order.  A draw (one 1024-thread workgroup) finds its chunk from the
+// chunk weights and then its entry inside that chunk, each time from a
+// fixed-order prefix sum over contiguous per-thread shares.  The residual of
+// a rejected row has its own, finer chunk sums.
 // The exponentials and sums are fp64 so that every decision (a comparison
 // with u times a probability or a cumulative weight) agrees with an exact
 // evaluation except within about 1e-15 (relative) of its threshold.
@@ -32,7 +35,14 @@
 namespace orthrus {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;        // statistics kernels
+constexpr int kDrawThreads = 1024;   // draw kernels (one workgroup per draw)
+
+struct RowNorm {       // a row's maximum and normaliser
+  double Z;
+  float M;
+  int pad;
+};
 
 struct SeqState {      // per sequence, after the acceptance test
   double Za, Zd;       // normalisers of row j (AR, draft views)
@@ -50,11 +60,20 @@ struct StatsArgs {
   double inv_t;
 };
 
+struct NormArgs {
+  const float* cm;
+  const double* cs;
+  double* cw;          // [rows][nchunks]: chunk weights relative to the row maximum
+  RowNorm* rn;         // [rows]
+  int rows, nchunks;
+  double inv_t;
+};
+
 struct SampleArgs {
   const float* z;
   const float* u;      // [rows]
-  const float* cm;
-  const double* cs;
+  const double* cw;
+  const RowNorm* rn;
   int32_t* out;        // [rows]
   int V, chunk, nchunks;
   double inv_t;
@@ -65,14 +84,13 @@ struct DecideArgs {
   const float* za;     // [B*K][V] AR view
   const int32_t* draft;
   const float* u_acc;  // [B][K]
-  const float* cm;     // [2*B*K][nchunks]: draft rows, then AR rows
-  const double* cs;
+  const RowNorm* rn;   // [2*B*K]: draft rows, then AR rows
   int32_t* tokens;     // [B][K]
   int32_t* n_acc;
   int32_t* n_emit;
   int32_t* next_anchor;
   SeqState* seq;       // [B]
-  int B, K, V, nchunks;
+  int B, K, V;
   double inv_t;
 };
 
@@ -80,13 +98,13 @@ struct ResidualArgs {
   const float* zd;
   const float* za;
   const float* u_res;  // [B][K]
-  const float* cm;
-  const double* cs;
+  const double* cw;    // for the fallback draw from p
+  const RowNorm* rn;
   const SeqState* seq;
-  double* rs;          // [B][nchunks] residual chunk sums
+  double* rs;          // [B][rchunks] residual chunk sums
   int32_t* tokens;
   int32_t* next_anchor;
-  int B, K, V, chunk, nchunks;
+  int B, K, V, chunk, nchunks, rchunk, rchunks;
   double inv_t;
 };
 
@@ -94,8 +112,8 @@ __device__ __forceinline__ double wexp(float z, float m, double inv_t) {
   return exp((double(z) - double(m)) * inv_t);
 }
 
-// Sum (or max) over the workgroup in a fixed order: wavefront butterflies,
-// then the four wavefront results in order.
+// Sum (or max) over a 256-thread workgroup in a fixed order: wavefront
+// butterflies, then the four wavefront results in order.
 __device__ double block_sum(double x, double* red) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
@@ -114,94 +132,111 @@ __device__ float block_max(float x, float* red) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// A row's maximum and normaliser from its chunk statistics, in chunk order.
-__device__ void row_norm(const float* cm, const double* cs, int nchunks, double inv_t, float* M, double* Z) {
-  float m = -INFINITY;
-  for (int c = 0; c < nchunks; ++c) m = fmaxf(m, cm[c]);
-  double z = 0.0;
-  for (int c = 0; c < nchunks; ++c) z += cs[c] * wexp(cm[c], m, inv_t);
-  *M = m;
-  *Z = z;
+// Inclusive and exclusive prefix sums of one value per thread over a
+// kDrawThreads workgroup, in a fixed order (a wavefront scan, then the
+// wavefront totals in order).  incl of thread t is bitwise the excl of thread
+// t+1, so "excl <= target < incl" holds for at most one thread.
+__device__ void block_scan(double x, double* excl, double* incl, double* total) {
+  __shared__ double wsum[kDrawThreads / 64];
+  __shared__ double wpre[kDrawThreads / 64 + 1];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  double v = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  double ve = __shfl_up(v, 1);
+  if (lane == 0) ve = 0.0;
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double run = 0.0;
+    for (int k = 0; k < kDrawThreads / 64; ++k) {
+      wpre[k] = run;
+      run = run + wsum[k];
+    }
+    wpre[kDrawThreads / 64] = run;
+  }
+  __syncthreads();
+  *incl = lane == 63 ? wpre[w + 1] : wpre[w] + v;
+  *excl = wpre[w] + ve;
+  *total = wpre[kDrawThreads / 64];
+  __syncthreads();
 }
 
-// Inverse-CDF draw over a row whose chunk weight sums are chunk_sum(c), with
-// element weights weight(v): the smallest v whose cumulative weight exceeds
-// u times the total.  Runs in one workgroup; every thread returns the token.
-// The chunk is found from the chunk sums in order, then thread k of the
-// workgroup sums its contiguous share of the chunk; the crossing thread
-// rescans its share with the same sequence of additions, so it finds the
-// crossing in its share.  If rounding leaves the target beyond every
-// cumulative weight, the last element of positive weight is taken.
-template <class ChunkSum, class Weight>
-__device__ int draw(ChunkSum chunk_sum, Weight weight, int nchunks, int chunk, int V, double u) {
-  __shared__ double part[kThreads];
-  __shared__ int sel[3];                           // chunk, thread, fallback token
+// Inverse-CDF draw in one kDrawThreads workgroup over a row whose chunk
+// weights are chunk_w(c) (c < nchunks, chunks of `chunk` entries) and whose
+// entry weights are weight(v): the smallest v whose cumulative weight exceeds
+// u times the total.  Chunks, then the chosen chunk's entries, are split into
+// contiguous per-thread shares; the one thread whose share holds the target
+// rescans it in order.  If rounding leaves the target at or beyond the end
+// of a share (or of the row), the share's last entry of positive weight is
+// taken.  Every thread returns the token.
+template <class ChunkW, class Weight>
+__device__ int draw(ChunkW chunk_w, Weight weight, int nchunks, int chunk, int V, double u) {
+  __shared__ int pick_s, last_s;
   __shared__ double rem_s;
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    double total = 0.0;
-    for (int c = 0; c < nchunks; ++c) total += chunk_sum(c);
-    double target = u * total, before = 0.0;
-    int cstar = -1, clast = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const double s = chunk_sum(c);
-      if (s > 0.0) clast = c;
-      if (cstar < 0 && before + s > target) cstar = c;
-      if (cstar < 0) before += s;
-    }
-    sel[0] = cstar < 0 ? clast : cstar;
-    // rounding at the very end of the row: no crossing, the last positive weight
-    rem_s = cstar < 0 ? INFINITY : target - before;
+  if (tid == 0) { pick_s = -1; last_s = -1; }
+  // ---- level 1: which chunk -------------------------------------------------
+  const int cpt = (nchunks + kDrawThreads - 1) / kDrawThreads;
+  const int c0 = min(tid * cpt, nchunks), c1 = min(c0 + cpt, nchunks);
+  double x = 0.0;
+  int lastc = -1;
+  for (int c = c0; c < c1; ++c) {
+    const double wc = chunk_w(c);
+    x += wc;
+    if (wc > 0.0) lastc = c;
   }
+  double excl, incl, total;
+  block_scan(x, &excl, &incl, &total);
+  const double target = u * total;
+  if (excl <= target && target < incl) {
+    double cum = excl;
+    int found = lastc;
+    for (int c = c0; c < c1; ++c) {
+      const double before = cum;
+      cum += chunk_w(c);
+      if (cum > target) { found = c; rem_s = target - before; break; }
+      if (c == lastc) rem_s = target - before;     // fallback: the share's last positive chunk
+    }
+    pick_s = found;
+  }
+  if (lastc >= 0) atomicMax(&last_s, lastc);
   __syncthreads();
-  const int c = sel[0];
-  const double rem = rem_s;
-  const int v0 = c * chunk, v1 = min(v0 + chunk, V);
-  const int per = (v1 - v0 + kThreads - 1) / kThreads;
-  const int a0 = v0 + tid * per, a1 = min(a0 + per, v1);
-  double mine = 0.0;
-  int last_pos = -1;
+  int cstar = pick_s;
+  double rem = rem_s;
+  if (cstar < 0) { cstar = last_s < 0 ? 0 : last_s; rem = INFINITY; }   // target beyond the row
+  __syncthreads();
+  if (tid == 0) { pick_s = -1; last_s = -1; }
+  __syncthreads();
+  // ---- level 2: which entry of chunk cstar -----------------------------------
+  const int v0 = cstar * chunk, v1 = min(v0 + chunk, V);
+  const int per = (v1 - v0 + kDrawThreads - 1) / kDrawThreads;
+  const int a0 = min(v0 + tid * per, v1), a1 = min(a0 + per, v1);
+  double y = 0.0;
+  int lastv = -1;
   for (int v = a0; v < a1; ++v) {
-    const double w = weight(v);
-    mine += w;
-    if (w > 0.0) last_pos = v;
+    const double wv = weight(v);
+    y += wv;
+    if (wv > 0.0) lastv = v;
   }
-  part[tid] = mine;
-  // the chunk's last positive weight, for the fallback
-  int lp = last_pos;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) lp = max(lp, __shfl_xor(lp, off));
-  if (tid == 0) sel[2] = -1;
-  __syncthreads();
-  if ((tid & 63) == 0) atomicMax(&sel[2], lp);
-  __syncthreads();
-  if (tid == 0) {
-    double before = 0.0;
-    int t = -1;
-    for (int k = 0; k < kThreads; ++k) {
-      if (before + part[k] > rem) { t = k; break; }
-      before += part[k];
-    }
-    sel[1] = t;
-    part[0] = before;                              // the cumulative weight before thread t
-  }
-  __syncthreads();
-  const int t = sel[1];
-  int token = sel[2];
-  __shared__ int tok_s;
-  if (t >= 0 && tid == t) {
-    const double before = part[0];
-    double run = 0.0;                              // the additions of `mine`, in its order
-    int found = -1;
+  double e2, i2, t2;
+  block_scan(y, &e2, &i2, &t2);
+  if (e2 <= rem && rem < i2) {
+    double cum = e2;
+    int found = lastv;
     for (int v = a0; v < a1; ++v) {
-      run += weight(v);
-      if (before + run > rem) { found = v; break; }
+      cum += weight(v);
+      if (cum > rem) { found = v; break; }
     }
-    tok_s = found >= 0 ? found : last_pos;          // (found always: before + mine > rem)
+    pick_s = found;
   }
+  if (lastv >= 0) atomicMax(&last_s, lastv);
   __syncthreads();
-  if (t >= 0) token = tok_s;
-  return token < 0 ? v0 : token;
+  int tok = pick_s >= 0 ? pick_s : last_s;
+  return tok < 0 ? v0 : tok;
 }
 
 // Chunk statistics of every row: m_c and s_c = sum exp((z - m_c) / T).
@@ -223,24 +258,39 @@ __global__ __launch_bounds__(kThreads) void sample_stats_kernel(StatsArgs a) {
   }
 }
 
-// One workgroup per row: out[row] = draw of softmax(z[row] / T) with u[row].
-__global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a) {
-  const int row = blockIdx.x;
+// One wavefront per row: the row maximum M, every chunk's weight
+// s_c exp((m_c - M) / T) and their sum Z (lane-strided, then a fixed butterfly).
+__global__ __launch_bounds__(kThreads) void row_norm_kernel(NormArgs a) {
+  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= a.rows) return;                       // uniform per wavefront
+  const int lane = threadIdx.x & 63;
   const float* cm = a.cm + size_t(row) * a.nchunks;
   const double* cs = a.cs + size_t(row) * a.nchunks;
-  __shared__ float M_s;
-  if (threadIdx.x == 0) {
-    float M;
-    double Z;
-    row_norm(cm, cs, a.nchunks, a.inv_t, &M, &Z);
-    M_s = M;
+  double* cw = a.cw + size_t(row) * a.nchunks;
+  float m = -INFINITY;
+  for (int c = lane; c < a.nchunks; c += 64) m = fmaxf(m, cm[c]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  double z = 0.0;
+  for (int c = lane; c < a.nchunks; c += 64) {
+    const double w = cs[c] * wexp(cm[c], m, a.inv_t);
+    cw[c] = w;
+    z += w;
   }
-  __syncthreads();
-  const float M = M_s;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+  if (lane == 0) a.rn[row] = RowNorm{z, m, 0};
+}
+
+// One workgroup per row: out[row] = draw of softmax(z[row] / T) with u[row].
+__global__ __launch_bounds__(kDrawThreads) void sample_draw_kernel(SampleArgs a) {
+  const int row = blockIdx.x;
+  const double* cw = a.cw + size_t(row) * a.nchunks;
+  const float M = a.rn[row].M;
   const float* z = a.z + size_t(row) * a.V;
   const double inv_t = a.inv_t;
-  const int tok = draw([&](int c) { return cs[c] * wexp(cm[c], M, inv_t); },
-                       [&](int v) { return wexp(z[v], M, inv_t); }, a.nchunks, a.chunk, a.V, double(a.u[row]));
+  const int tok = draw([&](int c) { return cw[c]; }, [&](int v) { return wexp(z[v], M, inv_t); },
+                       a.nchunks, a.chunk, a.V, double(a.u[row]));
   if (threadIdx.x == 0) a.out[row] = tok;
 }
 
@@ -252,17 +302,16 @@ __global__ __launch_bounds__(64) void sample_decide_kernel(DecideArgs a) {
   const int BK = a.B * a.K;
   bool reject = false;
   int32_t t = 0;
-  double Za = 0.0, Zd = 0.0;
-  float Ma = 0.f, Md = 0.f;
+  RowNorm nd{0.0, 0.f, 0}, na{0.0, 0.f, 0};
   if (i < a.K) {
-    const size_t rd = size_t(b) * a.K + i, ra = BK + rd;
-    row_norm(a.cm + rd * a.nchunks, a.cs + rd * a.nchunks, a.nchunks, a.inv_t, &Md, &Zd);
-    row_norm(a.cm + ra * a.nchunks, a.cs + ra * a.nchunks, a.nchunks, a.inv_t, &Ma, &Za);
+    const size_t rd = size_t(b) * a.K + i;
+    nd = a.rn[rd];
+    na = a.rn[BK + rd];
     t = a.draft[rd];
     double p = 0.0, q = 0.0;                       // a token outside the vocabulary has p = q = 0
     if (t >= 0 && t < a.V) {
-      p = wexp(a.za[rd * a.V + t], Ma, a.inv_t) / Za;
-      q = wexp(a.zd[rd * a.V + t], Md, a.inv_t) / Zd;
+      p = wexp(a.za[rd * a.V + t], na.M, a.inv_t) / na.Z;
+      q = wexp(a.zd[rd * a.V + t], nd.M, a.inv_t) / nd.Z;
     }
     reject = !(double(a.u_acc[rd]) * q < p);
   }
@@ -277,7 +326,7 @@ __global__ __launch_bounds__(64) void sample_decide_kernel(DecideArgs a) {
       a.seq[b] = SeqState{0.0, 0.0, 0.f, 0.f, a.K, 0};
     }
   }
-  if (i == j) a.seq[b] = SeqState{Za, Zd, Ma, Md, j, 0};
+  if (i == j) a.seq[b] = SeqState{na.Z, nd.Z, na.M, nd.M, j, 0};
 }
 
 struct Residual {
@@ -292,7 +341,8 @@ struct Residual {
   }
 };
 
-// Chunk sums of the residual max(0, p - q) of each sequence's rejected row.
+// Sums of the residual max(0, p - q) of each sequence's rejected row over
+// chunks of rchunk entries.
 __global__ __launch_bounds__(kThreads) void residual_stats_kernel(ResidualArgs a) {
   __shared__ double redd[4];
   const int b = blockIdx.y, c = blockIdx.x;
@@ -300,43 +350,43 @@ __global__ __launch_bounds__(kThreads) void residual_stats_kernel(ResidualArgs a
   if (st.j >= a.K) return;                         // uniform: nothing rejected
   const size_t row = size_t(b) * a.K + st.j;
   const Residual r{a.za + row * a.V, a.zd + row * a.V, st.Ma, st.Md, st.Za, st.Zd, a.inv_t};
-  const int v0 = c * a.chunk, v1 = min(v0 + a.chunk, a.V);
+  const int v0 = c * a.rchunk, v1 = min(v0 + a.rchunk, a.V);
   double s = 0.0;
   for (int v = v0 + threadIdx.x; v < v1; v += kThreads) s += r(v);
   s = block_sum(s, redd);
-  if (threadIdx.x == 0) a.rs[size_t(b) * a.nchunks + c] = s;
+  if (threadIdx.x == 0) a.rs[size_t(b) * a.rchunks + c] = s;
 }
 
 // One workgroup per sequence: the emitted token at the rejected row, a draw
 // of max(0, p - q) (of p if the residual is empty, which only rounding can
 // cause).
-__global__ __launch_bounds__(kThreads) void residual_draw_kernel(ResidualArgs a) {
+__global__ __launch_bounds__(kDrawThreads) void residual_draw_kernel(ResidualArgs a) {
   const int b = blockIdx.x;
   const SeqState st = a.seq[b];
   if (st.j >= a.K) return;
   const size_t row = size_t(b) * a.K + st.j;
-  const double* rs = a.rs + size_t(b) * a.nchunks;
-  __shared__ int empty_s;
-  if (threadIdx.x == 0) {
-    double tot = 0.0;
-    for (int c = 0; c < a.nchunks; ++c) tot += rs[c];
-    empty_s = !(tot > 0.0);
-  }
+  const double* rs = a.rs + size_t(b) * a.rchunks;
+  __shared__ double part[kDrawThreads / 64];
+  double x = 0.0;
+  for (int c = threadIdx.x; c < a.rchunks; c += kDrawThreads) x += rs[c];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
   __syncthreads();
+  bool empty = true;
+  for (int k = 0; k < kDrawThreads / 64; ++k) empty = empty && !(part[k] > 0.0);
   const double u = double(a.u_res[row]);
   int tok;
-  if (!empty_s) {
+  if (!empty) {
     const Residual r{a.za + row * a.V, a.zd + row * a.V, st.Ma, st.Md, st.Za, st.Zd, a.inv_t};
-    tok = draw([&](int c) { return rs[c]; }, r, a.nchunks, a.chunk, a.V, u);
+    tok = draw([&](int c) { return rs[c]; }, r, a.rchunks, a.rchunk, a.V, u);
   } else {
-    const size_t ra = size_t(a.B) * a.K + row;
-    const float* cm = a.cm + ra * a.nchunks;
-    const double* cs = a.cs + ra * a.nchunks;
+    const double* cw = a.cw + (size_t(a.B) * a.K + row) * a.nchunks;
     const float* z = a.za + row * a.V;
     const float M = st.Ma;
     const double inv_t = a.inv_t;
-    tok = draw([&](int c) { return cs[c] * wexp(cm[c], M, inv_t); },
-               [&](int v) { return wexp(z[v], M, inv_t); }, a.nchunks, a.chunk, a.V, u);
+    tok = draw([&](int c) { return cw[c]; }, [&](int v) { return wexp(z[v], M, inv_t); },
+               a.nchunks, a.chunk, a.V, u);
   }
   if (threadIdx.x == 0) {
     a.tokens[row] = tok;
@@ -347,6 +397,8 @@ __global__ __launch_bounds__(kThreads) void residual_draw_kernel(ResidualArgs a)
 struct Ws {
   float* cm;
   double* cs;
+  double* cw;
+  RowNorm* rn;
   SeqState* seq;
   double* rs;
 };
@@ -354,22 +406,32 @@ struct Ws {
 Ws carve(const SamplePlan& p, void* ws) {
   char* base = static_cast<char*>(ws);
   return Ws{reinterpret_cast<float*>(base + p.cm_off), reinterpret_cast<double*>(base + p.cs_off),
+            reinterpret_cast<double*>(base + p.cw_off), reinterpret_cast<RowNorm*>(base + p.rn_off),
             reinterpret_cast<SeqState*>(base + p.seq_off), reinterpret_cast<double*>(base + p.rs_off)};
+}
+
+hipError_t launch_stats(const SamplePlan& p, const Ws& w, const float* z0, const float* z1, int rows0,
+                        double inv_t, hipStream_t stream) {
+  StatsArgs s{z0, z1, w.cm, w.cs, rows0, p.rows, p.V, p.chunk, p.nchunks, inv_t};
+  hipError_t e = launch_kernel(&sample_stats_kernel, dim3(p.nchunks, p.rows), dim3(kThreads), stream, s);
+  if (e != hipSuccess) return e;
+  NormArgs n{w.cm, w.cs, w.cw, w.rn, p.rows, p.nchunks, inv_t};
+  return launch_kernel(&row_norm_kernel, dim3((p.rows + 3) / 4), dim3(kThreads), stream, n);
 }
 
 }  // namespace
 
 static_assert(sizeof(SeqState) == kSampleSeqBytes, "per-sequence state size");
+static_assert(sizeof(RowNorm) == kSampleRowBytes, "per-row state size");
 
 hipError_t launch_sample(const SamplePlan& p, const float* logits, float temperature, const float* u,
                          int32_t* out, void* ws, hipStream_t stream) {
   const Ws w = carve(p, ws);
   const double inv_t = 1.0 / double(temperature);
-  StatsArgs s{logits, logits, w.cm, w.cs, p.rows, p.rows, p.V, p.chunk, p.nchunks, inv_t};
-  hipError_t e = launch_kernel(&sample_stats_kernel, dim3(p.nchunks, p.rows), dim3(kThreads), stream, s);
+  hipError_t e = launch_stats(p, w, logits, logits, p.rows, inv_t, stream);
   if (e != hipSuccess) return e;
-  SampleArgs d{logits, u, w.cm, w.cs, out, p.V, p.chunk, p.nchunks, inv_t};
-  return launch_kernel(&sample_draw_kernel, dim3(p.rows), dim3(kThreads), stream, d);
+  SampleArgs d{logits, u, w.cw, w.rn, out, p.V, p.chunk, p.nchunks, inv_t};
+  return launch_kernel(&sample_draw_kernel, dim3(p.rows), dim3(kDrawThreads), stream, d);
 }
 
 hipError_t launch_accept_sampled(const SamplePlan& p, const float* logits_d, const float* logits_a,
@@ -378,18 +440,17 @@ hipError_t launch_accept_sampled(const SamplePlan& p, const float* logits_d, con
                                  int32_t* next_anchor, void* ws, hipStream_t stream) {
   const Ws w = carve(p, ws);
   const double inv_t = 1.0 / double(temperature);
-  StatsArgs s{logits_d, logits_a, w.cm, w.cs, B * K, 2 * B * K, p.V, p.chunk, p.nchunks, inv_t};
-  hipError_t e = launch_kernel(&sample_stats_kernel, dim3(p.nchunks, 2 * B * K), dim3(kThreads), stream, s);
+  hipError_t e = launch_stats(p, w, logits_d, logits_a, B * K, inv_t, stream);
   if (e != hipSuccess) return e;
-  DecideArgs d{logits_d, logits_a, draft, u_acc, w.cm, w.cs, tokens, n_acc, n_emit, next_anchor, w.seq,
-               B, K, p.V, p.nchunks, inv_t};
+  DecideArgs d{logits_d, logits_a, draft, u_acc, w.rn, tokens, n_acc, n_emit, next_anchor, w.seq,
+               B, K, p.V, inv_t};
   e = launch_kernel(&sample_decide_kernel, dim3(B), dim3(64), stream, d);
   if (e != hipSuccess) return e;
-  ResidualArgs r{logits_d, logits_a, u_res, w.cm, w.cs, w.seq, w.rs, tokens, next_anchor,
-                 B, K, p.V, p.chunk, p.nchunks, inv_t};
-  e = launch_kernel(&residual_stats_kernel, dim3(p.nchunks, B), dim3(kThreads), stream, r);
+  ResidualArgs r{logits_d, logits_a, u_res, w.cw, w.rn, w.seq, w.rs, tokens, next_anchor,
+                 B, K, p.V, p.chunk, p.nchunks, p.rchunk, p.rchunks, inv_t};
+  e = launch_kernel(&residual_stats_kernel, dim3(p.rchunks, B), dim3(kThreads), stream, r);
   if (e != hipSuccess) return e;
-  return launch_kernel(&residual_draw_kernel, dim3(B), dim3(kThreads), stream, r);
+  return launch_kernel(&residual_draw_kernel, dim3(B), dim3(kDrawThreads), stream, r);
 }
 
 }  // namespace orthrus
