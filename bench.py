@@ -409,8 +409,13 @@ def e2e(args, torch, dv, synth):
     res = {"e2e": "qwen3_8b_shape", "layers": cfg.layers, "hidden": cfg.hidden, "vocab": cfg.vocab,
            "block_k": K, "timing": "HIP graph replay", "contexts": []}
     reps = 10
-    for L in (int(x) for x in args.e2e_contexts.split(",")):
-        cache = ModelCache(cfg, L + (4 * reps + 8) * K + 256, dev)
+    # an e4m3 cache uses one scale (1/32) for every layer and head here: the
+    # timing does not depend on the values
+    scale8 = torch.full((cfg.layers, cfg.Hkv), 1.0 / 32, dtype=torch.float32, device=dev)
+    runs = [(int(x), kv) for x in args.e2e_contexts.split(",") for kv in ("bf16", "e4m3")]
+    for L, kv in runs:
+        cache = ModelCache(cfg, L + (4 * reps + 8) * K + 256, dev,
+                           kv_scales=(scale8, scale8) if kv == "e4m3" else None)
         cache.fill_random(L)
         tok = torch.zeros(1, dtype=torch.int64, device=dev)
         out = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -444,7 +449,7 @@ def e2e(args, torch, dv, synth):
             times[name] = e0.elapsed_time(e1) / (2 * reps)
         tg, to = times["greedy_step_ms"], times["orthrus_step_ms"]
         res["contexts"].append({
-            "context": L, "greedy_step_ms": round(tg, 3), "orthrus_step_ms": round(to, 3),
+            "context": L, "kv_cache": kv, "greedy_step_ms": round(tg, 3), "orthrus_step_ms": round(to, 3),
             "greedy_tokens_per_s": round(1e3 / tg, 1),
             "orthrus_tokens_per_s": {str(e): round(e * 1e3 / to, 1) for e in (5.39, 6.63)},
             "speedup_vs_greedy": {str(e): round(e * tg / to, 2) for e in (5.39, 6.63)},

@@ -13,7 +13,8 @@ view writes; the <mask> token is one extra embedding row.  Weights are random
 that the Orthrus loop reproduces greedy decoding.
 
 What runs where: block attention (both masks), the LM head fused with the
-argmax, acceptance and the all-layer commit are liborthrus kernels; the dense
+argmax, acceptance, the all-layer commit and (for an e4m3 cache) the
+quantisation of each layer's new K/V rows are liborthrus kernels; the dense
 layers are bf16 matrix products in torch (hipBLASLt) with fp32 accumulation,
 always on exactly 64 rows, so that a row's result never depends on how many
 real rows a call has; the RMSNorm reductions run on the same fixed shape;
@@ -35,15 +36,19 @@ PAGE = ob.ORTHRUS_PAGE_SIZE
 
 
 class ModelCache:
-    """All layers' K/V pools [layers, pages, Hkv, 16, D] (bf16), one sequence's
+    """All layers' K/V pools [layers, pages, Hkv, 16, D] (bf16, or e4m3 codes
+    with per-layer, per-KV-head fp32 scales [layers, Hkv]), one sequence's
     block table (a seeded permutation of the pool) and two device length
     buffers that alternate as input and output of the commit."""
 
-    def __init__(self, cfg, capacity: int, device, seed: int = 0):
+    def __init__(self, cfg, capacity: int, device, seed: int = 0, kv_scales=None):
         n_pages = -(-capacity // PAGE)
         shape = (cfg.layers, n_pages, cfg.Hkv, PAGE, cfg.D)
-        self.k = torch.zeros(shape, dtype=torch.bfloat16, device=device)
-        self.v = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+        self.fp8 = kv_scales is not None
+        dt = torch.uint8 if self.fp8 else torch.bfloat16
+        self.k = torch.zeros(shape, dtype=dt, device=device)
+        self.v = torch.zeros(shape, dtype=dt, device=device)
+        self.k_scale, self.v_scale = kv_scales if self.fp8 else (None, None)
         perm = np.random.default_rng(seed).permutation(n_pages).astype(np.int32)
         self.table = torch.from_numpy(perm[None, :]).to(device)
         self.lens = [torch.zeros(1, dtype=torch.int32, device=device),
@@ -56,18 +61,28 @@ class ModelCache:
         return self.lens[self.cur]
 
     def layer(self, i: int) -> ob.PagedKV:
+        if self.fp8:
+            return ob.PagedKV(self.k[i], self.v[i], self.table, self.lens[self.cur],
+                              k_scale=self.k_scale[i], v_scale=self.v_scale[i])
         return ob.PagedKV(self.k[i], self.v[i], self.table, self.lens[self.cur])
 
     def fill_random(self, L: int, seed: int = 0):
-        """Synthetic cache state of L tokens (N(0, 1) K/V) for timing."""
+        """Synthetic cache state of L tokens (N(0, 1) K/V, or e4m3 codes of
+        magnitude below 8 with random signs) for timing."""
         gen = torch.Generator(device=self.k.device).manual_seed(seed)
         for t in (self.k, self.v):
             for i in range(t.shape[0]):
-                t[i].copy_(torch.randn(t[i].shape, generator=gen, device=t.device))
+                if self.fp8:
+                    code = torch.randint(0, 0x50, t[i].shape, generator=gen, device=t.device, dtype=torch.int32)
+                    sign = torch.randint(0, 2, t[i].shape, generator=gen, device=t.device, dtype=torch.int32)
+                    t[i].copy_((code | (sign << 7)).to(torch.uint8))
+                else:
+                    t[i].copy_(torch.randn(t[i].shape, generator=gen, device=t.device))
         self.lens[self.cur].fill_(L)
 
     def commit(self, k_rows, v_rows, n_emit: torch.Tensor):
-        """k_rows, v_rows: bf16 [layers, 1, K, Hkv, D] of the AR view."""
+        """k_rows, v_rows: [layers, 1, K, Hkv, D] of the AR view, in the cache's
+        element type."""
         ob.orthrus_commit_kv(self.layer(0), k_rows, v_rows, n_emit, self.lens[1 - self.cur],
                              pool_layer_stride=self.k.stride(0))
         self.cur = 1 - self.cur
@@ -135,8 +150,8 @@ class DualViewModel:
     # ---- one forward over a block of rows -----------------------------------
     def forward(self, tokens: torch.Tensor, cache: ModelCache, view: str, mode: str):
         """tokens: int64 [n] (device) at positions L .. L+n-1, L = cache.length.
-        Returns (final hidden states bf16 [n, hidden], k_rows, v_rows bf16
-        [layers, 1, n, Hkv, D] of this view)."""
+        Returns (final hidden states bf16 [n, hidden], k_rows, v_rows
+        [layers, 1, n, Hkv, D] of this view in the cache's element type)."""
         c = self.cfg
         n = tokens.shape[0]
         assert n <= PAD_ROWS
@@ -158,6 +173,13 @@ class DualViewModel:
             q = self._rope(self._rms(q, self.w[p + "q_norm"]), pos).to(torch.bfloat16)[None].contiguous()
             k = self._rope(self._rms(k, self.w[p + "k_norm"]), pos).to(torch.bfloat16)[None].contiguous()
             v = v.contiguous()
+            if cache.fp8:
+                # the block's rows in the cache's format: attention reads, and
+                # the commit stores, exactly these codes
+                k8 = torch.empty(k.shape, dtype=torch.uint8, device=self.device)
+                v8 = torch.empty_like(k8)
+                ob.orthrus_quantize_kv(k, v, cache.k_scale[i], cache.v_scale[i], k8, v8)
+                k, v = k8, v8
             o = torch.empty_like(q)
             fn(cache.layer(i), q, k, v, o, max_ctx=max_ctx, workspace=ws)
             x = x + self._lin(o[0].view(n, qd), self.w[p + "wo" + sfx]).float()
@@ -194,8 +216,22 @@ class DualViewModel:
         cache.commit(k, v, n_emit)
 
     # ---- host-driven decoding (tests) -----------------------------------------
-    def new_cache(self, prompt_len: int, n_new: int, seed: int = 0) -> ModelCache:
-        return ModelCache(self.cfg, prompt_len + n_new + 2 * self.max_block + PAD_ROWS + PAGE, self.device, seed)
+    def new_cache(self, prompt_len: int, n_new: int, seed: int = 0, kv_scales=None) -> ModelCache:
+        return ModelCache(self.cfg, prompt_len + n_new + 2 * self.max_block + PAD_ROWS + PAGE, self.device, seed,
+                          kv_scales=kv_scales)
+
+    def calibrate_kv_scales(self, prompt: torch.Tensor, headroom: float = 2.0):
+        """Per-layer, per-KV-head e4m3 scales from the AR view's K/V on the first
+        (up to 64) prompt tokens: amax * headroom / 448 (static scales, as a
+        serving system calibrates them once)."""
+        blk = prompt[:PAD_ROWS]
+        cache = ModelCache(self.cfg, blk.shape[0] + PAD_ROWS + PAGE, self.device)
+        _, k, v = self.forward(blk, cache, "ar", "verify")
+        scales = []
+        for t in (k, v):                                      # [layers, 1, n, Hkv, D]
+            amax = t.float().abs().amax(dim=(1, 2, 4))        # [layers, Hkv]
+            scales.append((amax.clamp_min(1e-3) * headroom / 448.0).contiguous())
+        return tuple(scales)
 
     def prefill(self, prompt: torch.Tensor, cache: ModelCache) -> int:
         out = torch.empty(1, dtype=torch.int32, device=self.device)
@@ -206,8 +242,8 @@ class DualViewModel:
         self.greedy_token(hidden[-1:], out)
         return int(out.item())
 
-    def greedy(self, prompt: torch.Tensor, n: int, seed: int = 0):
-        cache = self.new_cache(prompt.shape[0], n, seed)
+    def greedy(self, prompt: torch.Tensor, n: int, seed: int = 0, kv_scales=None):
+        cache = self.new_cache(prompt.shape[0], n, seed, kv_scales)
         toks = [self.prefill(prompt, cache)]
         out = torch.empty(1, dtype=torch.int32, device=self.device)
         t0 = time.perf_counter()
@@ -216,10 +252,11 @@ class DualViewModel:
             toks.append(int(out.item()))
         return toks, time.perf_counter() - t0
 
-    def orthrus(self, prompt: torch.Tensor, n: int, K: int = 32, drafter=None, seed: int = 0):
+    def orthrus(self, prompt: torch.Tensor, n: int, K: int = 32, drafter=None, seed: int = 0, kv_scales=None):
         """drafter(emitted_tokens, K) -> host int32 [K] overrides the diffusion
-        view's draft (the draft pass still runs)."""
-        cache = self.new_cache(prompt.shape[0], n, seed)
+        view's draft (the draft pass still runs).  kv_scales (k, v fp32
+        [layers, Hkv]) selects an e4m3 cache."""
+        cache = self.new_cache(prompt.shape[0], n, seed, kv_scales)
         toks = [self.prefill(prompt, cache)]
         anchor = torch.tensor([toks[0]], device=self.device)
         d, a = (torch.empty((1, K), dtype=torch.int32, device=self.device) for _ in range(2))

@@ -5,7 +5,8 @@ matrix products with fp32 accumulation.  The Orthrus loop must emit exactly
 the tokens of plain greedy decoding of the same model: with its own
 (untrained) drafter, with a teacher drafter that proposes the greedy
 continuation corrupted at a geometric position, and with a drafter that is
-always wrong."""
+always wrong; and the same with an e4m3 KV cache (scales calibrated on the
+prompt), whose block rows are quantised before both passes."""
 import numpy as np
 import pytest
 import torch
@@ -67,3 +68,40 @@ def test_orthrus_wrong_drafter_matches_greedy(setup):
                                    drafter=lambda out, k: (np.array(ref[len(out):len(out) + k]) + 1) % V)
     assert toks == ref[:12]
     assert emits == [1] * 11
+
+
+@pytest.fixture(scope="module")
+def fp8_ref(setup):
+    model, prompt, _ = setup
+    scales = model.calibrate_kv_scales(prompt)
+    ref, _ = model.greedy(prompt, 32 + K, kv_scales=scales)
+    print(f"greedy with the e4m3 cache: {ref[:12]} ...", flush=True)
+    return scales, ref
+
+
+def test_fp8_cache_teacher_drafter_matches_greedy(setup, fp8_ref):
+    model, prompt, _ = setup
+    scales, ref = fp8_ref
+    assert len(set(ref[:32])) > 8
+    rng = np.random.default_rng(5)
+    V = model.cfg.vocab
+
+    def teacher(out, k):
+        e = len(out)
+        d = np.array(ref[e:e + k], dtype=np.int32)
+        m = min(int(rng.geometric(0.15)) - 1, k)
+        if m < k:
+            d[m] = (d[m] + 1) % V
+        return d
+
+    toks, emits, _ = model.orthrus(prompt, 32, K, drafter=teacher, kv_scales=scales)
+    print(f"e4m3 teacher drafter: {len(emits)} steps, mean emitted {np.mean(emits):.2f}", flush=True)
+    assert toks == ref[:32]
+    assert len(emits) < 16
+
+
+def test_fp8_cache_own_drafter_matches_greedy(setup, fp8_ref):
+    model, prompt, _ = setup
+    scales, ref = fp8_ref
+    toks, emits, _ = model.orthrus(prompt, 12, K, kv_scales=scales)
+    assert toks == ref[:12]
