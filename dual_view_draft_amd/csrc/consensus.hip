@@ -121,16 +121,34 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(FinalArgs a) {
 }
 
 // One workgroup per sequence: its four wavefronts reduce the K rows' chunk
-// keys (rows w, w+4, ...), then wavefront 0 runs the prefix scan with lane i
-// owning block row i (K <= 64).
+// keys (rows w, w+4, ...; every load of a wavefront's rows is issued before
+// the first reduction, so they cost one memory round trip), then wavefront 0
+// runs the prefix scan with lane i owning block row i (K <= 64).
 __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
+  constexpr int RPW = ORTHRUS_MAX_BLOCK / 4;     // rows per wavefront
   __shared__ int32_t tok_s[64];
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int i = w; i < a.K; i += 4) {
-    const size_t row = size_t(b) * a.K + i;
-    const unsigned long long best = row_key(a.keys + row * a.nchunks, a.nchunks, lane);
-    if (lane == 0) tok_s[i] = key_index(best);
+  unsigned long long best[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) best[r] = 0ull;
+  for (int c0 = 0; c0 < a.nchunks; c0 += 64) {   // 64 chunks at a time: one predicated load per row
+    unsigned long long k[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int i = w + 4 * r;
+      k[r] = (i < a.K && c0 + lane < a.nchunks) ? a.keys[(size_t(b) * a.K + i) * a.nchunks + c0 + lane] : 0ull;
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) best[r] = umax64(best[r], k[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int i = w + 4 * r;
+    if (i < a.K) {                               // uniform per wavefront
+      const unsigned long long m = wave_max(best[r]);
+      if (lane == 0) tok_s[i] = key_index(m);
+    }
   }
   __syncthreads();
   if (w != 0) return;
