@@ -51,8 +51,25 @@ struct LmArgs {
   const uint16_t* w;         // [V][hidden] bf16
   float* logits;             // [rows][V] fp32, or null (not written)
   unsigned long long* keys;  // [rows][nwg]
-  int rows, hidden, V, nwg;
+  int rows, hidden, V, nwg, nrc;
 };
+
+// Workgroup -> (vocabulary range wg, row chunk rc).  Workgroups are dealt to
+// the eight XCDs in turn (linear id mod 8).  The row chunks of one vocabulary
+// range take consecutive slots on one XCD, so they stream the same weight
+// rows at about the same time and share them through that XCD's L2 instead
+// of each reading them from HBM.
+__device__ __forceinline__ void lm_tile(const LmArgs& a, int* wg, int* rc) {
+  const int L = blockIdx.x;
+  if (a.nrc == 1 || (a.nwg & 7)) {
+    *wg = L % a.nwg;
+    *rc = L / a.nwg;
+    return;
+  }
+  const int x = L & 7, m = L >> 3;
+  *wg = (m / a.nrc) * 8 + x;
+  *rc = m - (m / a.nrc) * a.nrc;
+}
 
 constexpr int VB = 256;               // vocabulary rows per block (8 wavefronts x 32)
 constexpr int KT = kLmKTile;          // hidden elements per tile
@@ -91,8 +108,9 @@ __device__ __forceinline__ void write_row_keys(const LmArgs& a, unsigned long lo
 __global__ __launch_bounds__(512, 1) void lmhead_kernel(LmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ring[NS * STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t sink[512];   // target of the spare loads
-  const int wg = blockIdx.x;
-  const int row0 = blockIdx.y * RC;
+  int wg, rc;
+  lm_tile(a, &wg, &rc);
+  const int row0 = rc * RC;
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, col = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -199,8 +217,9 @@ constexpr int R2_MAX_KT = kLmRegHidden / R2_KT;
 __global__ __launch_bounds__(512, 1) void lmhead_rows_kernel(LmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ring[R2_NS * R2_TILE];
   static_assert(8 * 32 * 32 * 4 == R2_TILE * 2, "a block's partial sums fill one stage");
-  const int wg = blockIdx.x;
-  const int row0 = blockIdx.y * RC;
+  int wg, rc;
+  lm_tile(a, &wg, &rc);
+  const int row0 = rc * RC;
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, col = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -306,10 +325,10 @@ __global__ __launch_bounds__(512, 1) void lmhead_rows_kernel(LmArgs a) {
 hipError_t launch_lmhead(const LmHeadPlan& p, const void* hidden, const void* weight, float* logits,
                          void* ws, hipStream_t stream) {
   LmArgs a{static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(weight), logits,
-           static_cast<unsigned long long*>(ws), p.rows, p.hidden, p.V, p.nwg};
-  if (p.hidden <= kLmRegHidden)
-    return launch_kernel(&lmhead_rows_kernel, dim3(p.nwg, p.nrc), dim3(512), stream, a);
-  return launch_kernel(&lmhead_kernel, dim3(p.nwg, p.nrc), dim3(512), stream, a);
+           static_cast<unsigned long long*>(ws), p.rows, p.hidden, p.V, p.nwg, p.nrc};
+  const dim3 grid(unsigned(int64_t(p.nwg) * p.nrc));
+  if (p.hidden <= kLmRegHidden) return launch_kernel(&lmhead_rows_kernel, grid, dim3(512), stream, a);
+  return launch_kernel(&lmhead_kernel, grid, dim3(512), stream, a);
 }
 
 }  // namespace orthrus
