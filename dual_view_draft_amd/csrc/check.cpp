@@ -172,8 +172,14 @@ bool plan_lmhead(int rows, int hidden, int V, LmHeadPlan* p, std::string* why) {
     return no("hidden must be a multiple of 64 in [64, 2^20]");
   if (int64_t(rows) * V > (int64_t(1) << 40)) return no("rows * vocab too large");
   p->rows = rows; p->hidden = hidden; p->V = V;
-  p->nwg = V < kLmWorkgroups ? V : kLmWorkgroups;
-  p->nrc = int(ceil_div(rows, kLmRowChunk));
+  p->gemm = rows > kLmGemmRows;
+  if (p->gemm) {
+    p->nwg = int(ceil_div(V, kLmGemmVocabTile));
+    p->nrc = int(ceil_div(rows, kLmGemmRowTile));
+  } else {
+    p->nwg = V < kLmWorkgroups ? V : kLmWorkgroups;
+    p->nrc = int(ceil_div(rows, kLmRowChunk));
+  }
   p->ws_bytes = size_t(round_up(int64_t(rows > 0 ? rows : 1) * p->nwg * 8, 256));
   return true;
 }

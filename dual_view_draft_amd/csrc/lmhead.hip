@@ -320,12 +320,151 @@ __global__ __launch_bounds__(512, 1) void lmhead_rows_kernel(LmArgs a) {
   write_row_keys(a, best, reinterpret_cast<unsigned long long*>(ring), wg, row0, wave, half, col);
 }
 
+// GEMM-tiled variant for many query rows (batched decoding: B*K rows).
+// There the product is no longer bound by one pass over the weights: it is a
+// dense contraction (M = rows, N = vocabulary, K = hidden) whose weights
+// every row tile must see.  Each workgroup owns one output tile of 256
+// vocabulary rows x 128 query rows and runs the whole hidden dimension in
+// tiles of 64 (48 KiB per ring stage: the weight tile and the query tile,
+// three stages).  Wavefront w computes vocabulary rows 64(w%4) .. +63 x query
+// rows 64(w/4) .. +63, four 32x32x16 bf16 MFMA blocks per k-step.  The row
+// tiles of one vocabulary tile are dealt to one XCD back to back (workgroup
+// id mod 8 picks the XCD), so the weight tile comes from HBM once and from
+// L2 for the other row tiles.  The epilogue turns each query row's 256
+// logits into one (value, index) key per workgroup: keys[row][vocab tile].
+constexpr int G_VB = 256, G_RB = 128, G_KT = 64, G_NS = 3;
+constexpr int G_W = G_VB * G_KT, G_H = G_RB * G_KT;   // elements per stage
+constexpr int G_STAGE = G_W + G_H;                      // 48 KiB
+constexpr int G_LPT = 6;                                // 4 weight + 2 query loads per wavefront
+
+__global__ __launch_bounds__(512, 1) void lmhead_gemm_kernel(LmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t ring[G_NS * G_STAGE];
+  // workgroup -> (vocabulary tile, row tile); the grid is padded to a
+  // multiple of 8 vocabulary tiles
+  const int L = blockIdx.x;
+  const int m = L >> 3;
+  const int vt = (m / a.nrc) * 8 + (L & 7);
+  const int rt = m - (m / a.nrc) * a.nrc;
+  if (vt >= a.nwg) return;                       // uniform: padding
+  const int v0 = vt * G_VB, row0 = rt * G_RB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = wave & 3, wr = wave >> 2;
+  const int nkt = a.hidden / G_KT;
+
+  // Loads of hidden tile kt into stage st: weight rows 32w + 8i + l/8
+  // (i < 4) and query rows 16w + 8i + l/8 (i < 2), granule l%8 of the LDS
+  // row holding logical granule (l%8) ^ swz(row).  Rows outside the
+  // vocabulary or past the last query row, and tiles past the end, load the
+  // 16 zero bytes, so every step issues G_LPT loads.
+  const int lr = lane >> 3, lp = lane & 7;
+  auto issue_tile = [&](int kt, uint16_t* st) {
+    const bool live = kt < nkt;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wave * 32 + i * 8 + lr;
+      const int v = v0 + r;
+      const void* src = (live && v < a.V)
+                            ? static_cast<const void*>(a.w + size_t(v) * a.hidden + kt * G_KT + (lp ^ swz(r)) * 8)
+                            : static_cast<const void*>(g_lm_zero16);
+      load_lds16(src, lds_addr(st + (wave * 32 + i * 8) * G_KT));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = wave * 16 + i * 8 + lr;
+      const int hr = row0 + r;
+      const void* src = (live && hr < a.rows)
+                            ? static_cast<const void*>(a.h + size_t(hr) * a.hidden + kt * G_KT + (lp ^ swz(r)) * 8)
+                            : static_cast<const void*>(g_lm_zero16);
+      load_lds16(src, lds_addr(st + G_W + (wave * 16 + i * 8) * G_KT));
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < G_NS - 1; ++k) issue_tile(k, ring + k * G_STAGE);
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+  for (int kt = 0; kt < nkt; ++kt) {
+    wait_vmcnt<(G_NS - 2) * G_LPT>();    // tile kt has landed for this wavefront
+    lds_barrier();                       // ... for every wavefront; stage of kt-1 is free
+    const int tn = kt + G_NS - 1;
+    issue_tile(tn, ring + (tn % G_NS) * G_STAGE);
+    const uint16_t* wt = ring + (kt % G_NS) * G_STAGE;
+    const uint16_t* ht = wt + G_W;
+#pragma unroll
+    for (int ks = 0; ks < G_KT / 16; ++ks) {
+      const int g = ks * 2 + half;
+      bf16x8 av[2], bv[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int ra = wv * 64 + x * 32 + col;
+        av[x] = *reinterpret_cast<const bf16x8*>(wt + ra * G_KT + ((g ^ swz(ra)) * 8));
+        const int rb = wr * 64 + x * 32 + col;
+        bv[x] = *reinterpret_cast<const bf16x8*>(ht + rb * G_KT + ((g ^ swz(rb)) * 8));
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x], bv[y], acc[x][y], 0, 0, 0);
+    }
+  }
+
+  // lane l, block (x, y), value v: vocabulary row v0 + 64 wv + 32 x + 8(v/4)
+  // + 4 half + v%4, query row row0 + 64 wr + 32 y + col
+  unsigned long long best[2] = {0ull, 0ull};
+#pragma unroll
+  for (int y = 0; y < 2; ++y) {
+    const int row = row0 + wr * 64 + y * 32 + col;
+    const bool row_ok = row < a.rows;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int vb = v0 + wv * 64 + x * 32 + 4 * half;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int vi = vb + 8 * (v >> 2) + (v & 3);
+        if (vi < a.V) {
+          best[y] = umax64(best[y], make_key(acc[x][y][v], vi));
+          if (a.logits && row_ok) a.logits[size_t(row) * a.V + vi] = acc[x][y][v];
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();                        // trailing zero-tile loads have landed
+  lds_barrier();                          // every wavefront is done with the ring
+  unsigned long long* red = reinterpret_cast<unsigned long long*>(ring);   // [4 vocabulary groups][128 rows]
+#pragma unroll
+  for (int y = 0; y < 2; ++y) {
+    unsigned long long k = best[y];
+    const auto lo = __builtin_amdgcn_permlane32_swap(uint32_t(k), uint32_t(k), false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap(uint32_t(k >> 32), uint32_t(k >> 32), false, false);
+    k = umax64((static_cast<unsigned long long>(hi[0]) << 32) | lo[0],
+               (static_cast<unsigned long long>(hi[1]) << 32) | lo[1]);
+    if (half == 0) red[wv * G_RB + wr * 64 + y * 32 + col] = k;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): the LDS writes are done
+  lds_barrier();
+  if (tid < G_RB && row0 + tid < a.rows) {
+    unsigned long long k = red[tid];
+#pragma unroll
+    for (int g = 1; g < 4; ++g) k = umax64(k, red[g * G_RB + tid]);
+    a.keys[size_t(row0 + tid) * a.nwg + vt] = k;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_lmhead(const LmHeadPlan& p, const void* hidden, const void* weight, float* logits,
                          void* ws, hipStream_t stream) {
   LmArgs a{static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(weight), logits,
            static_cast<unsigned long long*>(ws), p.rows, p.hidden, p.V, p.nwg, p.nrc};
+  if (p.gemm) {
+    const dim3 grid(unsigned((int64_t(p.nwg) + 7) / 8 * 8 * p.nrc));
+    return launch_kernel(&lmhead_gemm_kernel, grid, dim3(512), stream, a);
+  }
   const dim3 grid(unsigned(int64_t(p.nwg) * p.nrc));
   if (p.hidden <= kLmRegHidden) return launch_kernel(&lmhead_rows_kernel, grid, dim3(512), stream, a);
   return launch_kernel(&lmhead_kernel, grid, dim3(512), stream, a);

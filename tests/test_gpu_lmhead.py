@@ -112,3 +112,53 @@ def test_lmhead_accept_matches_oracle(lib, n_acc):
     assert np.array_equal(ar, a)
     assert np.array_equal(na, ref_na) and np.array_equal(ne, ref_ne) and np.array_equal(nx, ref_nx)
     assert np.all(na == n_acc)
+
+
+# more than 64 rows take the GEMM-tiled kernel (256 vocabulary x 128 row tiles)
+@pytest.mark.parametrize("R,Hd,V", [(65, 192, 300), (129, 256, 5000), (300, 1024, 20011), (200, 8192, 3000)])
+def test_gemm_tiled_planted_winner(lib, R, Hd, V):
+    from synth import make_lmhead_case
+    c = make_lmhead_case(R * 13 + V, R, Hd, V)
+    tok, logits = run(lib, c)
+    check_against_oracle(c, tok, logits, exact_tokens=True)
+    assert np.array_equal(tok, c.targets)
+
+
+def test_gemm_tiled_random_rows(lib):
+    from synth import make_lmhead_case
+    c = make_lmhead_case(77, 160, 2048, 30000, plant=False)
+    tok, logits = run(lib, c)
+    check_against_oracle(c, tok, logits, exact_tokens=False)
+
+
+def test_gemm_tiled_8b_vocabulary_batch_16(lib):
+    """B*K = 512 rows (batch 16, K 32) against the 8B vocabulary; the tokens of
+    the logits-free path equal those of the launch that also writes logits."""
+    from synth import make_lmhead_case
+    c = make_lmhead_case(9, 512, 4096, 151936)
+    tok, logits = run(lib, c)
+    check_against_oracle(c, tok, logits, exact_tokens=True)
+    tok2, _ = run(lib, c, with_logits=False)
+    assert np.array_equal(tok, tok2)
+
+
+def test_gemm_tiled_accept_batch_16(lib):
+    from oracle import accept
+    from synth import make_lmhead_case
+    B, K, Hd, V = 16, 32, 1024, 30000
+    c = make_lmhead_case(101, B * K, Hd, V)
+    a = c.targets.reshape(B, K)
+    d = a.copy()
+    rng = np.random.default_rng(4)
+    for b in range(B):
+        m = int(rng.integers(0, K + 1))
+        if m < K:
+            d[b, m] = (a[b, m] + 1) % V
+    h = bf16_dev(c.hidden).view(B, K, Hd)
+    outs = [torch.full(s, -7, dtype=torch.int32, device="cuda") for s in ((B, K), (B,), (B,), (B,))]
+    lib.orthrus_lmhead_accept(h, bf16_dev(c.weight), i32_dev(d), *outs)
+    torch.cuda.synchronize()
+    ar, na, ne, nx = (t.cpu().numpy() for t in outs)
+    ref_na, ref_ne, ref_nx = accept(d, a)
+    assert np.array_equal(ar, a)
+    assert np.array_equal(na, ref_na) and np.array_equal(ne, ref_ne) and np.array_equal(nx, ref_nx)
