@@ -14,8 +14,10 @@
 // index in the low word).  The maximum key is the maximum value with the
 // lowest index, whatever order the reduction runs in, so the result is
 // deterministic and independent of the launch shape.  A small second kernel
-// reduces the chunk keys of each row (argmax) or of each sequence's K rows
-// and runs the prefix scan with one wavefront ballot (accept).
+// reduces the chunk keys of each row (argmax, one wavefront per row) or of
+// each sequence's K rows and runs the prefix scan with one wavefront ballot
+// (accept; there a small group of lanes reduces each row, so that one
+// workgroup handles all K rows in a single pass).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -48,7 +50,7 @@ struct AcceptArgs {
   int32_t* n_acc;
   int32_t* n_emit;
   int32_t* next_anchor;
-  int B, K, nchunks;
+  int B, K, nchunks, lpr;
 };
 
 __device__ __forceinline__ unsigned long long wave_max(unsigned long long k) {
@@ -104,55 +106,81 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(PartialArgs a) {
   }
 }
 
-// Reduce the chunk keys of one row with one wavefront (lane c reads chunk c).
-__device__ __forceinline__ unsigned long long row_key(const unsigned long long* keys, int nchunks, int lane) {
-  unsigned long long best = 0ull;
-  for (int c = lane; c < nchunks; c += 64) best = umax64(best, keys[c]);
-  return wave_max(best);
+// Lanes that reduce one row's chunk keys: a power of two (1..64) that leaves
+// each lane kpl keys or fewer up to 64 kpl chunks, so a row costs one round
+// trip of loads and log2(lanes) shuffle steps, and a wavefront reduces
+// 64 / lanes rows at once.
+int lanes_per_row(int nchunks, int kpl) {
+  const int want = (nchunks + kpl - 1) / kpl;
+  int lpr = 1;
+  while (lpr < want && lpr < 64) lpr <<= 1;
+  return lpr;
 }
 
-// One wavefront per row.
+// Maximum over the aligned group of lpr lanes (lpr a power of two <= 64).
+__device__ __forceinline__ unsigned long long group_max(unsigned long long k, int lpr) {
+  for (int off = lpr >> 1; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(k), off);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(k >> 32), off);
+    k = umax64(k, (static_cast<unsigned long long>(hi) << 32) | lo);
+  }
+  return k;
+}
+
+// One row's maximum key, reduced by the lpr lanes of its group (sub = this
+// lane's place in the group); every lane of the group receives it.
+template <int KPL>
+__device__ __forceinline__ unsigned long long row_key(const unsigned long long* keys, int nchunks, int sub,
+                                                      int lpr) {
+  unsigned long long best = 0ull;
+  for (int c0 = 0; c0 < nchunks; c0 += KPL * lpr) {
+    unsigned long long k[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int c = c0 + j * lpr + sub;
+      k[j] = c < nchunks ? keys[c] : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) best = umax64(best, k[j]);
+  }
+  return group_max(best, lpr);
+}
+
+// One wavefront per row (lane c reads chunks c, c + 64, ...): the rows of a
+// call run side by side on many CUs.
 __global__ __launch_bounds__(256) void argmax_final_kernel(FinalArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;                     // uniform per wavefront
   const int lane = threadIdx.x & 63;
-  const unsigned long long best = row_key(a.keys + size_t(row) * a.nchunks, a.nchunks, lane);
+  const unsigned long long* keys = a.keys + size_t(row) * a.nchunks;
+  unsigned long long best = 0ull;
+  for (int c = lane; c < a.nchunks; c += 64) best = umax64(best, keys[c]);
+  best = wave_max(best);
   if (lane == 0) a.out[row] = key_index(best);
 }
 
-// One workgroup per sequence: its four wavefronts reduce the K rows' chunk
-// keys (rows w, w+4, ...; every load of a wavefront's rows is issued before
-// the first reduction, so they cost one memory round trip), then wavefront 0
-// runs the prefix scan with lane i owning block row i (K <= 64).
-__global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
-  constexpr int RPW = ORTHRUS_MAX_BLOCK / 4;     // rows per wavefront
+// One workgroup of THREADS threads per sequence: groups of lpr lanes reduce
+// the K rows' chunk keys (THREADS / lpr rows at a time, KPL keys per lane
+// and round trip), then wavefront 0 runs the prefix scan with lane i owning
+// block row i (K <= 64).  256 threads serve when they cover all K rows in one
+// pass (few chunks per row, as on the logits path); otherwise 1024.
+template <int THREADS, int KPL>
+__global__ __launch_bounds__(THREADS) void accept_kernel(AcceptArgs a) {
   __shared__ int32_t tok_s[64];
   const int b = blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  unsigned long long best[RPW];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) best[r] = 0ull;
-  for (int c0 = 0; c0 < a.nchunks; c0 += 64) {   // 64 chunks at a time: one predicated load per row
-    unsigned long long k[RPW];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int i = w + 4 * r;
-      k[r] = (i < a.K && c0 + lane < a.nchunks) ? a.keys[(size_t(b) * a.K + i) * a.nchunks + c0 + lane] : 0ull;
-    }
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) best[r] = umax64(best[r], k[r]);
-  }
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int i = w + 4 * r;
-    if (i < a.K) {                               // uniform per wavefront
-      const unsigned long long m = wave_max(best[r]);
-      if (lane == 0) tok_s[i] = key_index(m);
+  const int sub = threadIdx.x % a.lpr;
+  const int rows_per_pass = THREADS / a.lpr;
+  for (int i0 = 0; i0 < a.K; i0 += rows_per_pass) {
+    const int i = i0 + threadIdx.x / a.lpr;
+    if (i < a.K) {                               // whole groups take the same branch
+      const unsigned long long m =
+          row_key<KPL>(a.keys + (size_t(b) * a.K + i) * a.nchunks, a.nchunks, sub, a.lpr);
+      if (sub == 0) tok_s[i] = key_index(m);
     }
   }
   __syncthreads();
-  if (w != 0) return;
-  const int i = lane;
+  if (threadIdx.x >= 64) return;
+  const int i = threadIdx.x;
   int32_t tok = 0;
   bool mismatch = false;
   if (i < a.K) {
@@ -188,8 +216,11 @@ hipError_t launch_argmax_keys(const unsigned long long* keys, int rows, int nchu
 hipError_t launch_accept_keys(const unsigned long long* keys, int nchunks, const int32_t* draft, int B,
                               int K, int32_t* a, int32_t* n_acc, int32_t* n_emit, int32_t* next_anchor,
                               hipStream_t stream) {
-  AcceptArgs x{keys, draft, a, n_acc, n_emit, next_anchor, B, K, nchunks};
-  return launch_kernel(&accept_kernel, dim3(B), dim3(256), stream, x);
+  // 256 threads when they cover the K rows in one pass, else 1024
+  AcceptArgs x{keys, draft, a, n_acc, n_emit, next_anchor, B, K, nchunks, lanes_per_row(nchunks, 8)};
+  if (K * x.lpr <= 256) return launch_kernel(&accept_kernel<256, 8>, dim3(B), dim3(256), stream, x);
+  x.lpr = lanes_per_row(nchunks, 16);
+  return launch_kernel(&accept_kernel<1024, 16>, dim3(B), dim3(1024), stream, x);
 }
 
 hipError_t launch_argmax(const ArgmaxPlan& p, const float* logits, int32_t* out, void* ws,
