@@ -131,13 +131,18 @@ struct SplitCfg {
   static_assert(LPR >= 1, "a wavefront's 8 rows fill at least one 1 KiB load");
 
   // Physical 16-byte granule of logical granule c in tile row t is c ^ swizzle(t).
+  // LDS has 64 four-byte banks; a 16-byte read serves 16 consecutive lanes per
+  // cycle and an 8-byte (transposing) read 32 consecutive lanes.
   // K: the 16 rows read by 16 consecutive lanes (one per row, same logical
-  // granule) land on distinct LDS banks.  V: granule pairs stay together (the
-  // transposing reads take 8 or 16 bytes of one pair) and the rows that one
-  // transposing read gathers land on distinct banks.
+  // granule) land on distinct banks.  V: granule pairs stay together (the
+  // transposing reads take 8 or 16 bytes of one pair), and the 4 rows that 32
+  // lanes of one transposing read gather (64 bytes of d each) land on distinct
+  // banks: with 256-byte rows (bf16, head_dim 128) each row's 4 granules move
+  // to their own quarter of the row.
   __device__ static __forceinline__ int kswz(int t) { return FP8 ? (t >> 1) & 7 : t & (KG - 1); }
   __device__ static __forceinline__ int vswz(int t) {
-    return FP8 ? 2 * (((t >> 1) & 1) | ((t >> 2) & 2)) : 2 * (t & (KG / 2 - 1));
+    if constexpr (FP8) return 2 * (((t >> 1) & 1) | ((t >> 2) & 2));
+    return KG == 16 ? 4 * (t & 3) : 2 * (t & 3);
   }
 };
 

@@ -67,6 +67,10 @@ def _accept_gpu(dv, logits_a, d):
     ("ragged16", 4, 16, 32, 151936, "geometric"),
     ("odd_vocab", 5, 3, 5, 1001, "uniform"),
     ("k64", 6, 2, 64, 4096, "uniform"),
+    # 38 chunk keys per row and 48 rows: more rows than one 256-thread pass
+    # holds, so the 1024-thread reduction runs
+    ("k48_big_vocab", 7, 1, 48, 151936, "geometric"),
+    ("k64_big_vocab", 8, 2, 64, 151936, "uniform"),
 ])
 def test_accept_matches_oracle(lib, name, seed, B, K, V, dist):
     from oracle import accept, argmax_rows
