@@ -542,23 +542,50 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   if (half == 0) *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) = f32x2{M, l_tot};
 }
 
+// Sum of x over the lanes l, l ^ off (off a power of two <= 32): the pair is
+// added in the same order in both lanes, so they hold the same bits.
+__device__ __forceinline__ float pair_sum(float x, int off) {
+  if (off == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if (off == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const float y = __shfl_xor(x, off);
+  return (threadIdx.x & off) ? y + x : x + y;
+}
+__device__ __forceinline__ float pair_max(float x, int off) {
+  if (off == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  if (off == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return fmaxf(x, __shfl_xor(x, off));
+}
+
 // Merge the split partials of every output row:
 //   out = sum_s w_s l_s Ohat_s / sum_s w_s l_s,  w_s = 2^(m_s - M),  M = max_s m_s,
-// with Ohat_s = O_s / l_s (bf16).  One wavefront per output row: lane s % 64
-// holds split s's (m, l); D/8 lanes cover the row (8 values, 16 bytes each)
-// and the 64/(D/8) lane groups take interleaved splits in increasing order;
-// the group sums are added in group order.  The first batch of partial rows
-// is loaded together with the (m, l) pairs, since Ohat_s does not depend on
-// M, so a row with up to 8 splits per lane group costs one memory round
-// trip.  Splits a row cannot see contribute exact zeros, so the result does
-// not depend on how many splits the call had.
+// with Ohat_s = O_s / l_s (bf16).  One wavefront per output row: D/8 lanes
+// cover the row (8 values, 16 bytes each) and the 64/(D/8) lane groups take
+// interleaved splits, U per group and batch.  Every lane loads the (m, l) of
+// its own splits with their partial rows, so a row with up to U splits per
+// lane group costs one memory round trip, and takes the weights in the lane;
+// the maximum and the group sums cross lanes only in log2(groups) swap steps
+// (permlane swaps for lane distances 16 and 32).  Batches after the first
+// rescale the running sums when the maximum grows.  Splits a row cannot see
+// contribute exact zeros, so the result does not depend on how many splits
+// the call had.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
   constexpr int TPR = D / 8;      // lanes per row slice
   constexpr int SG = 64 / TPR;    // split groups per wavefront
   constexpr int U = 8;            // splits per lane group per batch
-  constexpr int BATCH = U * SG;   // splits per batch (divides 64)
-  static_assert(64 % BATCH == 0, "a batch stays inside one group of 64 splits");
+  constexpr int BATCH = U * SG;   // splits per batch
   const int lane = threadIdx.x & 63;
   const int orow = blockIdx.x * 4 + (threadIdx.x >> 6);   // (b, i, h) flattened
   if (orow >= a.B * a.K * a.Hq) return;                    // uniform per wavefront
@@ -578,76 +605,74 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
   const uint16_t* po = a.part_o + prow0 * D + d0;
   const size_t ml_stride = size_t(a.rpc) * 2, o_stride = size_t(a.rpc) * D;
 
-  // Loads are bounded by the call's split count only, so they need not wait
-  // for the sequence length; slots of splits >= ns hold nothing of this call
-  // and are discarded by selects (never multiplied: they may hold any bits).
-  auto load_ml = [&](int s) {
-    f32x2 e = {-__builtin_inff(), 0.f};
-    if (s < a.nsplit) e = *reinterpret_cast<const f32x2*>(ml + s * ml_stride);
-    return e;
-  };
-  auto load_batch = [&](int j0, u32x4* raw) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + u * SG + sg;
-      raw[u] = u32x4{0u, 0u, 0u, 0u};
-      if (j < a.nsplit) raw[u] = *reinterpret_cast<const u32x4*>(po + j * o_stride);
-    }
-  };
-
-  // one round trip: (m, l) of splits 0..63 and the first batch of partial rows
-  f32x2 e = load_ml(lane);
+  // Loads read slots of the call's splits only (indices past the last one
+  // read the last one again); slots of splits >= ns hold nothing of this
+  // call and are skipped (never multiplied: they may hold any bits).
+  f32x2 e[U];
   u32x4 raw[U];
-  load_batch(0, raw);
-  const int L = clamp_len(a.seq_lens[b], a.max_ctx);
-  const int ns = (L + a.K + a.split - 1) / a.split;
-  float M = lane < ns ? e[0] : -__builtin_inff();
-  for (int s0 = 64; s0 < ns; s0 += 64) {
-    const float m = load_ml(s0 + lane)[0];
-    if (s0 + lane < ns) M = fmaxf(M, m);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  const float M_use = (M == -__builtin_inff()) ? 0.f : M;
-
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.f;
-  float wl = lane < ns ? __builtin_amdgcn_exp2f(e[0] - M_use) * e[1] : 0.f;   // w_s l_s, s = lane
-  for (int j0 = 0; j0 < ns; j0 += BATCH) {
-    if (j0 > 0) {
-      if ((j0 & 63) == 0) {                       // next group of 64 splits
-        e = load_ml(j0 + lane);
-        wl = j0 + lane < ns ? __builtin_amdgcn_exp2f(e[0] - M_use) * e[1] : 0.f;
-      }
-      load_batch(j0, raw);
-    }
+  auto load_batch = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = j0 + u * SG + sg;
-      const float w = __shfl(wl, j & 63);
-      if (j < ns) {
+      const size_t j = size_t(min(j0 + u * SG + sg, a.nsplit - 1));
+      e[u] = *reinterpret_cast<const f32x2*>(ml + j * ml_stride);
+      raw[u] = *reinterpret_cast<const u32x4*>(po + j * o_stride);
+    }
+  };
+  const int L_raw = a.seq_lens[b];
+  load_batch(0);
+  // The empty asm statements take the loaded values as operands: the first
+  // batch is in flight together with the sequence length (one round trip)
+  // instead of being issued once the length is known.
+#pragma unroll
+  for (int u = 0; u < U; ++u) asm volatile("" ::"v"(e[u]), "v"(raw[u]));
+  asm volatile("" ::"v"(L_raw) : "memory");
+  const int L = clamp_len(L_raw, a.max_ctx);
+  const int ns = (L + a.K + a.split - 1) / a.split;
+
+  float M = -__builtin_inff();     // running maximum of m_s over the batches so far
+  float lsum = 0.f;                // this lane's sum of w_s l_s, relative to M
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < ns; j0 += BATCH) {
+    if (j0 > 0) load_batch(j0);
+    float mb = -__builtin_inff();
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (j0 + u * SG + sg < ns) mb = fmaxf(mb, e[u][0]);
+#pragma unroll
+    for (int off = TPR; off < 64; off <<= 1) mb = pair_max(mb, off);
+    const float Mn = fmaxf(M, mb);
+    const float Mu = (Mn == -__builtin_inff()) ? 0.f : Mn;
+    if (j0 > 0 && M != -__builtin_inff() && Mn != M) {      // uniform: rescale earlier batches
+      const float sc = __builtin_amdgcn_exp2f(M - Mu);
+      lsum *= sc;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] *= sc;
+    }
+    M = Mn;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j0 + u * SG + sg < ns) {
+        const float w = __builtin_amdgcn_exp2f(e[u][0] - Mu) * e[u][1];
+        lsum += w;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           acc[2 * q] += w * bf16_lo(raw[u][q]);
           acc[2 * q + 1] += w * bf16_hi(raw[u][q]);
         }
-        lsum += w;
       }
     }
   }
-  float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float ltot = 0.f;
+  // sum the lane groups: lanes l and l ^ off hold the same d
 #pragma unroll
-  for (int k = 0; k < SG; ++k) {
-    const int src = (lane % TPR) + k * TPR;
+  for (int off = TPR; off < 64; off <<= 1) {
+    lsum = pair_sum(lsum, off);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) tot[q] += __shfl(acc[q], src);
-    ltot += __shfl(lsum, src);
+    for (int q = 0; q < 8; ++q) acc[q] = pair_sum(acc[q], off);
   }
   if (sg != 0) return;
-  const float inv = 1.0f / ltot;
-  const u32x4 packed = {pack_bf16x2(tot[0] * inv, tot[1] * inv), pack_bf16x2(tot[2] * inv, tot[3] * inv),
-                        pack_bf16x2(tot[4] * inv, tot[5] * inv), pack_bf16x2(tot[6] * inv, tot[7] * inv)};
+  const float inv = 1.0f / lsum;
+  const u32x4 packed = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                        pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
   *reinterpret_cast<u32x4*>(a.out + size_t(orow) * D + d0) = packed;
 }
 
