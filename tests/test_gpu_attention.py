@@ -110,6 +110,33 @@ def test_group_size_8_rows_over_128(lib):
         compare(run(lib, c, mode), oracle(c, mode), f"G=8 {mode}")
 
 
+def _random_shape(i):
+    """Seeded random attention shape: batch 1-3, K 1-64, 1-4 KV heads, group
+    1-16, head_dim 64 or 128, cached lengths 0-1500 (ragged), a split size
+    from the library's choice down to one tile, and sometimes a max_ctx above
+    the longest sequence (splits past every sequence exit)."""
+    rng = np.random.default_rng(1000 + i)
+    B = int(rng.integers(1, 4))
+    K = int(rng.choice([1, 2, 7, 8, 13, 32, 33, 64]))
+    Hkv = int(rng.integers(1, 5))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    D = int(rng.choice([64, 128]))
+    lens = [int(x) for x in rng.integers(0, 1501, size=B)]
+    split = int(rng.choice([0, 64, 128, 320]))
+    slack = int(rng.choice([0, 0, 700]))
+    return B, K, G * Hkv, Hkv, D, lens, split, slack
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_shapes(lib, i):
+    B, K, Hq, Hkv, D, lens, split, slack = _random_shape(i)
+    c = case(2000 + i, B, K, Hq, Hkv, D, lens, sharp=bool(i % 2), extra_pages_per_seq=(slack + 15) // 16)
+    print(f"random {i}: B={B} K={K} Hq={Hq} Hkv={Hkv} D={D} lens={lens} split={split} slack={slack}", flush=True)
+    for mode in ("draft", "verify"):
+        got = run(lib, c, mode, max_ctx=max(lens) + slack, split=split)
+        compare(got, oracle(c, mode), f"random {i} {mode}")
+
+
 def test_last_row_draft_equals_verify_bitwise(lib):
     c = case(8, 2, 32, 32, 8, 128, [1500, 64], sharp=True)
     d, v = run(lib, c, "draft"), run(lib, c, "verify")
