@@ -20,10 +20,11 @@
 //   depend on K or on the other rows present.
 //
 // Memory path: tiles go HBM -> LDS directly (16-byte global_load_lds per lane,
-// 1 KiB per wavefront instruction) through a 4-stage LDS ring, so three tiles
-// (96 KiB for head_dim 128) are in flight while one is computed.  Each
-// wavefront fetches half of one page of K and of V per tile; page ids come
-// from the block table once per split.
+// 1 KiB per wavefront instruction) through a 5-stage LDS ring (9 stages for
+// the e4m3 cache): while tile t's P.V and tile t+1's scores are computed,
+// three tiles (96 KiB for bf16 head_dim 128) are in flight.  Each wavefront
+// fetches half of one page of K and of V per tile; page ids come from the
+// block table once per split.
 //
 // Compute per tile (wavefront w: rows 32*(w%4)+0..31, tokens 32*(w/4)+0..31):
 //   S^T[token][row] = K . Q^T   32x32x16 bf16 MFMA, A = K from LDS, B = Q in
