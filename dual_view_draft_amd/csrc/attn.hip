@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
+#include <utility>
 
 #include "check.h"
 #include "launch.h"
@@ -48,6 +50,16 @@
 
 namespace orthrus {
 namespace {
+
+// f(std::integral_constant<int, k>) for k = 0 .. N-1, expanded at compile time.
+template <typename F, int... Ks>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Ks...>) {
+  (f(std::integral_constant<int, Ks>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -373,11 +385,13 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   f32x16 sacc = f32x16{};
   if (wave_rows) sacc = qk(stage(0));
 
-  for (int t0 = 0; t0 < ntiles; t0 += NS) {
-#pragma unroll
-    for (int k = 0; k < NS; ++k) {
+  // One step of the ring: returns false past the last tile.  The NS steps of
+  // a pass are unrolled so that every stage number is a constant; for the
+  // e4m3 ring (NS = 9) the compiler keeps a plain loop rolled, so there they
+  // are expanded by template.
+  auto step = [&](const int t0, const int k) __attribute__((always_inline)) -> bool {
       const int t = t0 + k;
-      if (t >= ntiles) break;                                      // uniform
+      if (t >= ntiles) return false;                               // uniform
       const int ts = start + t * kTile;
       float m_use = 0.f;
       if (wave_rows) {
@@ -461,6 +475,15 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
         }
         sacc = snext;
       }
+      return true;
+  };
+  for (int t0 = 0; t0 < ntiles; t0 += NS) {
+    if constexpr (FP8) {
+      static_for<NS>([&](auto kc) { step(t0, decltype(kc)::value); });
+    } else {
+#pragma unroll
+      for (int k = 0; k < NS; ++k)
+        if (!step(t0, k)) break;
     }
   }
 
