@@ -193,6 +193,10 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
   const int rg = wave & 3, th = wave >> 2;      // row group, token half
 
+  // The K/V stream is read once: the bf16 cache's tiles load with the
+  // non-temporal policy (faster); for the e4m3 cache, whose pass is bound by
+  // arithmetic, it measured no better, and the default policy stays.
+  constexpr bool kStreamNT = !FP8;
   const int start = s * a.split;
   // Table index of this wavefront's page of tile t_idx, clamped to the row so
   // it can be read before the sequence length is known.
@@ -284,8 +288,8 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
     if (ts + kTile <= L) {                       // uniform: whole tile from the cache
 #pragma unroll
       for (int j = 0; j < LPR; ++j) {
-        load_lds16(kbase + koff[j], lds_addr(dst + j * 1024));
-        load_lds16(vbase + voff[j], lds_addr(dst + TILE_BYTES + j * 1024));
+        load_lds16<kStreamNT>(kbase + koff[j], lds_addr(dst + j * 1024));
+        load_lds16<kStreamNT>(vbase + voff[j], lds_addr(dst + TILE_BYTES + j * 1024));
       }
     } else {
 #pragma unroll
@@ -298,8 +302,8 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
           ks = p < N ? static_cast<const void*>(kblk + (p - L) * blk_row + (lgran ^ C::kswz(t)) * 16) : g_zero16;
           vs = p < N ? static_cast<const void*>(vblk + (p - L) * blk_row + (lgran ^ C::vswz(t)) * 16) : g_zero16;
         }
-        load_lds16(ks, lds_addr(dst + j * 1024));
-        load_lds16(vs, lds_addr(dst + TILE_BYTES + j * 1024));
+        load_lds16<kStreamNT>(ks, lds_addr(dst + j * 1024));
+        load_lds16<kStreamNT>(vs, lds_addr(dst + TILE_BYTES + j * 1024));
       }
     }
   };

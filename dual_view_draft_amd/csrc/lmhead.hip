@@ -143,7 +143,8 @@ __global__ __launch_bounds__(512, 1) void lmhead_kernel(LmArgs a) {
       const int c = lp ^ swz(r);
       const void* src = v < v1 ? static_cast<const void*>(a.w + size_t(v) * a.hidden + kt * KT + c * 8)
                                : static_cast<const void*>(g_lm_zero16);
-      load_lds16(src, lds_addr(st + (wave * 32 + i * 8) * KT));
+      if (a.nrc == 1) load_lds16<true>(src, lds_addr(st + (wave * 32 + i * 8) * KT));   // read once
+      else load_lds16(src, lds_addr(st + (wave * 32 + i * 8) * KT));
     }
     if (wave < 4) {
       const int r = wave * 8 + lr;
@@ -261,7 +262,8 @@ __global__ __launch_bounds__(512, 1) void lmhead_rows_kernel(LmArgs a) {
       const void* src = (live && v < v1 && k < a.hidden)
                             ? static_cast<const void*>(a.w + size_t(v) * a.hidden + k)
                             : static_cast<const void*>(g_lm_zero16);
-      load_lds16(src, lds_addr(st + r * R2_KT));
+      if (a.nrc == 1) load_lds16<true>(src, lds_addr(st + r * R2_KT));   // read once
+      else load_lds16(src, lds_addr(st + r * R2_KT));
     }
   };
 #pragma unroll
