@@ -172,8 +172,20 @@ bool plan_lmhead(int rows, int hidden, int V, LmHeadPlan* p, std::string* why) {
     return no("hidden must be a multiple of 64 in [64, 2^20]");
   if (int64_t(rows) * V > (int64_t(1) << 40)) return no("rows * vocab too large");
   p->rows = rows; p->hidden = hidden; p->V = V;
-  p->gemm = rows > kLmGemmRows;
-  if (p->gemm) {
+  p->gemm = 0;
+  if (rows > kLmGemmRows) {
+    // Both GEMM kernels run one workgroup per CU (256 CUs).  A wide tile does
+    // twice a narrow tile's work in about 1.87 times its time (measured at
+    // hidden 4096, vocabulary 151936), so the wide kernel is chosen only
+    // where its workgroups fill the rounds of 256 better.
+    const int64_t narrow = ceil_div(V, kLmGemmVocabTile) * ceil_div(rows, kLmGemmRowTile);
+    const int64_t wide = ceil_div(V, kLmGemmWideVocabTile) * ceil_div(rows, kLmGemmWideRowTile);
+    p->gemm = ceil_div(wide, 256) * 187 < ceil_div(narrow, 256) * 100 ? 2 : 1;
+  }
+  if (p->gemm == 2) {
+    p->nwg = int(ceil_div(V, kLmGemmWideVocabTile));
+    p->nrc = int(ceil_div(rows, kLmGemmWideRowTile));
+  } else if (p->gemm == 1) {
     p->nwg = int(ceil_div(V, kLmGemmVocabTile));
     p->nrc = int(ceil_div(rows, kLmGemmRowTile));
   } else {

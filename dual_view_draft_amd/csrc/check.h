@@ -41,13 +41,15 @@ constexpr int kLmRowChunk = 32;
 constexpr int kLmKTile = 64;
 constexpr int kLmRegHidden = 5120;   // up to this hidden size the query rows live in registers
 
-constexpr int kLmGemmRows = 64;       // more rows than this take the GEMM-tiled kernel
+constexpr int kLmGemmRows = 64;       // more rows than this take a GEMM-tiled kernel
 constexpr int kLmGemmVocabTile = 256;
 constexpr int kLmGemmRowTile = 128;
+constexpr int kLmGemmWideVocabTile = 256;
+constexpr int kLmGemmWideRowTile = 256;
 
 struct LmHeadPlan {
   int rows = 0, hidden = 0, V = 0;
-  bool gemm = false;     // GEMM-tiled kernel (many rows)
+  int gemm = 0;          // 0: rows kernel; 1: GEMM 256 x 128 tiles; 2: GEMM 256 x 256 tiles
   int nwg = 0;           // vocabulary ranges (or tiles) = argmax key chunks per row
   int nrc = 0;           // row chunks of kLmRowChunk rows (or row tiles)
   size_t ws_bytes = 0;   // keys [rows][nwg] (8 bytes each)

@@ -322,25 +322,62 @@ __global__ __launch_bounds__(512, 1) void lmhead_rows_kernel(LmArgs a) {
   write_row_keys(a, best, reinterpret_cast<unsigned long long*>(ring), wg, row0, wave, half, col);
 }
 
-// GEMM-tiled variant for many query rows (batched decoding: B*K rows).
+// GEMM-tiled variants for many query rows (batched decoding: B*K rows).
 // There the product is no longer bound by one pass over the weights: it is a
 // dense contraction (M = rows, N = vocabulary, K = hidden) whose weights
-// every row tile must see.  Each workgroup owns one output tile of 256
-// vocabulary rows x 128 query rows and runs the whole hidden dimension in
-// tiles of 64 (48 KiB per ring stage: the weight tile and the query tile,
-// three stages).  Wavefront w computes vocabulary rows 64(w%4) .. +63 x query
-// rows 64(w/4) .. +63, four 32x32x16 bf16 MFMA blocks per k-step.  The row
-// tiles of one vocabulary tile are dealt to one XCD back to back (workgroup
-// id mod 8 picks the XCD), so the weight tile comes from HBM once and from
-// L2 for the other row tiles.  The epilogue turns each query row's 256
-// logits into one (value, index) key per workgroup: keys[row][vocab tile].
-constexpr int G_VB = 256, G_RB = 128, G_KT = 64, G_NS = 3;
-constexpr int G_W = G_VB * G_KT, G_H = G_RB * G_KT;   // elements per stage
-constexpr int G_STAGE = G_W + G_H;                      // 48 KiB
-constexpr int G_LPT = 6;                                // 4 weight + 2 query loads per wavefront
+// every row tile must see.  Each workgroup (8 wavefronts) owns one output
+// tile of VB vocabulary rows x RB query rows and runs the whole hidden
+// dimension in tiles of GKT elements through an NS-stage LDS ring (the weight
+// tile and the query tile per stage, NS - 1 tiles in flight).  The
+// wavefronts form an NWV x NWR grid; each computes XB x YB blocks of
+// 32x32x16 bf16 MFMA products (32 XB vocabulary rows x 32 YB query rows) per
+// k-step.  The row tiles of one vocabulary tile are dealt to one XCD back to
+// back (workgroup id mod 8 picks the XCD), so the weight tile comes from HBM
+// once and from L2 for the other row tiles.  The epilogue turns each query
+// row's VB logits into one (value, index) key per workgroup:
+// keys[row][vocabulary tile].
+//
+// Two instances:
+// - narrow: 256 x 128 tiles, 64 x 64 per wavefront, 64-element hidden tiles,
+//   three 48 KiB stages;
+// - wide: 256 x 256 tiles, 128 x 64 per wavefront, 32-element hidden tiles,
+//   four 32 KiB stages.  It loads 1.5 times fewer bytes into LDS per product
+//   and reads 6 operand blocks from LDS per 8 products instead of 4 per 4,
+//   which makes a workgroup about 7 % cheaper per product.
+// The host takes the one whose workgroups fill rounds of 256 CUs better.
+// Both keep one fp32 running sum per logit over 16-element products in
+// increasing hidden order, so they agree bit for bit.  The row-streaming
+// kernel instead adds eight per-wavefront partial sums, so a row's logits
+// may differ in the last bits between a call of at most 64 rows and a
+// larger one (and a near-tie may then pick another token).
+template <int NWV_, int NWR_, int XB_, int YB_, int GKT_, int GNS_>
+struct GemmCfg {
+  static constexpr int NWV = NWV_, NWR = NWR_, XB = XB_, YB = YB_, GKT = GKT_, GNS = GNS_;
+  static constexpr int VB = NWV * XB * 32, RB = NWR * YB * 32;
+  static constexpr int ROWB = GKT * 2;                 // bytes per tile row
+  static constexpr int GR = GKT / 8;                   // 16-byte granules per tile row
+  static constexpr int RPL = 1024 / ROWB;              // tile rows per 1 KiB load instruction
+  static constexpr int RPB = 256 / ROWB;               // tile rows per 256-byte bank row
+  static constexpr int W = VB * GKT, H = RB * GKT;    // elements per stage
+  static constexpr int STAGE = W + H;
+  static constexpr int WCH = VB / RPL, HCH = RB / RPL; // 1 KiB chunks per stage
+  static constexpr int LPT = (WCH + HCH) / 8;          // loads per wavefront per tile
+  static constexpr int WLPT = WCH / 8;                 // ... of which weight loads
+  static_assert(NWV * NWR == 8 && GKT % 16 == 0 && WCH % 8 == 0 && HCH % 8 == 0, "tile shape");
+  static_assert(GNS >= 3, "ring depth");
+  // Granule c of tile row r sits at c ^ ((r / RPB) mod GR): the 16 rows one
+  // 16-lane group of an operand read touches fall on distinct LDS banks.
+  static __device__ __forceinline__ int swz(int r) { return (r / RPB) % GR; }
+};
+using GemmNarrow = GemmCfg<4, 2, 2, 2, 64, 3>;
+using GemmWide = GemmCfg<2, 4, 4, 2, 32, 4>;
+static_assert(GemmNarrow::VB == kLmGemmVocabTile && GemmNarrow::RB == kLmGemmRowTile &&
+              GemmWide::VB == kLmGemmWideVocabTile && GemmWide::RB == kLmGemmWideRowTile, "host tiles");
 
-__global__ __launch_bounds__(512, 1) void lmhead_gemm_kernel(LmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ring[G_NS * G_STAGE];
+template <class C>
+__device__ __forceinline__ void lmhead_gemm_body(const LmArgs& a) {
+  constexpr int NWV = C::NWV, NWR = C::NWR, XB = C::XB, YB = C::YB, GKT = C::GKT, GNS = C::GNS;
+  __shared__ __attribute__((aligned(16))) uint16_t ring[GNS * C::STAGE];
   // workgroup -> (vocabulary tile, row tile); the grid is padded to a
   // multiple of 8 vocabulary tiles
   const int L = blockIdx.x;
@@ -348,83 +385,93 @@ __global__ __launch_bounds__(512, 1) void lmhead_gemm_kernel(LmArgs a) {
   const int vt = (m / a.nrc) * 8 + (L & 7);
   const int rt = m - (m / a.nrc) * a.nrc;
   if (vt >= a.nwg) return;                       // uniform: padding
-  const int v0 = vt * G_VB, row0 = rt * G_RB;
+  const int v0 = vt * C::VB, row0 = rt * C::RB;
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, col = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wv = wave & 3, wr = wave >> 2;
-  const int nkt = a.hidden / G_KT;
+  const int wv = wave % NWV, wr = wave / NWV;
+  const int nkt = a.hidden / GKT;
 
-  // Loads of hidden tile kt into stage st: weight rows 32w + 8i + l/8
-  // (i < 4) and query rows 16w + 8i + l/8 (i < 2), granule l%8 of the LDS
-  // row holding logical granule (l%8) ^ swz(row).  Rows outside the
-  // vocabulary or past the last query row, and tiles past the end, load the
-  // 16 zero bytes, so every step issues G_LPT loads.
-  const int lr = lane >> 3, lp = lane & 7;
+  // Loads of hidden tile kt into stage st: wavefront w fills the 1 KiB
+  // chunks w + 8i of the stage (weight rows first, then query rows), lane l
+  // row RPL c + l / GR and granule l % GR of the LDS row, which holds logical
+  // granule (l % GR) ^ swz(row).  Rows outside the vocabulary or past the
+  // last query row, and tiles past the end, load the 16 zero bytes, so every
+  // step issues LPT loads.
+  const int lr = lane / C::GR, lp = lane % C::GR;
   auto issue_tile = [&](int kt, uint16_t* st) {
     const bool live = kt < nkt;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wave * 32 + i * 8 + lr;
-      const int v = v0 + r;
-      const void* src = (live && v < a.V)
-                            ? static_cast<const void*>(a.w + size_t(v) * a.hidden + kt * G_KT + (lp ^ swz(r)) * 8)
-                            : static_cast<const void*>(g_lm_zero16);
-      load_lds16(src, lds_addr(st + (wave * 32 + i * 8) * G_KT));
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = wave * 16 + i * 8 + lr;
-      const int hr = row0 + r;
-      const void* src = (live && hr < a.rows)
-                            ? static_cast<const void*>(a.h + size_t(hr) * a.hidden + kt * G_KT + (lp ^ swz(r)) * 8)
-                            : static_cast<const void*>(g_lm_zero16);
-      load_lds16(src, lds_addr(st + G_W + (wave * 16 + i * 8) * G_KT));
+    for (int i = 0; i < C::LPT; ++i) {
+      const int c = wave + 8 * i;
+      const void* src = g_lm_zero16;
+      if (i < C::WLPT) {
+        const int r = c * C::RPL + lr;
+        const int v = v0 + r;
+        if (live && v < a.V) src = a.w + size_t(v) * a.hidden + kt * GKT + (lp ^ C::swz(r)) * 8;
+      } else {
+        const int r = (c - C::WCH) * C::RPL + lr;
+        const int hr = row0 + r;
+        if (live && hr < a.rows) src = a.h + size_t(hr) * a.hidden + kt * GKT + (lp ^ C::swz(r)) * 8;
+      }
+      load_lds16(src, lds_addr(st + c * C::RPL * GKT));
     }
   };
 #pragma unroll
-  for (int k = 0; k < G_NS - 1; ++k) issue_tile(k, ring + k * G_STAGE);
+  for (int k = 0; k < GNS - 1; ++k) issue_tile(k, ring + k * C::STAGE);
 
-  f32x16 acc[2][2];
+  f32x16 acc[XB][YB];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < XB; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+    for (int y = 0; y < YB; ++y) acc[x][y] = f32x16{};
   for (int kt = 0; kt < nkt; ++kt) {
-    wait_vmcnt<(G_NS - 2) * G_LPT>();    // tile kt has landed for this wavefront
+    wait_vmcnt<(GNS - 2) * C::LPT>();    // tile kt has landed for this wavefront
     lds_barrier();                       // ... for every wavefront; stage of kt-1 is free
-    const int tn = kt + G_NS - 1;
-    issue_tile(tn, ring + (tn % G_NS) * G_STAGE);
-    const uint16_t* wt = ring + (kt % G_NS) * G_STAGE;
-    const uint16_t* ht = wt + G_W;
+    const int tn = kt + GNS - 1;
+    issue_tile(tn, ring + (tn % GNS) * C::STAGE);
+    const uint16_t* wt = ring + (kt % GNS) * C::STAGE;
+    const uint16_t* ht = wt + C::W;
+    // All operand reads of the tile go out first, so their LDS latency is
+    // paid once per tile rather than once per k-step (the scheduling barrier
+    // keeps the compiler from sinking them between the products).
+    constexpr int NKS = GKT / 16;
+    bf16x8 av[NKS][XB], bv[NKS][YB];
 #pragma unroll
-    for (int ks = 0; ks < G_KT / 16; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
       const int g = ks * 2 + half;
-      bf16x8 av[2], bv[2];
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int ra = wv * 64 + x * 32 + col;
-        av[x] = *reinterpret_cast<const bf16x8*>(wt + ra * G_KT + ((g ^ swz(ra)) * 8));
-        const int rb = wr * 64 + x * 32 + col;
-        bv[x] = *reinterpret_cast<const bf16x8*>(ht + rb * G_KT + ((g ^ swz(rb)) * 8));
+      for (int x = 0; x < XB; ++x) {
+        const int ra = wv * XB * 32 + x * 32 + col;
+        av[ks][x] = *reinterpret_cast<const bf16x8*>(wt + ra * GKT + ((g ^ C::swz(ra)) * 8));
       }
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x], bv[y], acc[x][y], 0, 0, 0);
+      for (int y = 0; y < YB; ++y) {
+        const int rb = wr * YB * 32 + y * 32 + col;
+        bv[ks][y] = *reinterpret_cast<const bf16x8*>(ht + rb * GKT + ((g ^ C::swz(rb)) * 8));
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int x = 0; x < XB; ++x)
+#pragma unroll
+        for (int y = 0; y < YB; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks][x], bv[ks][y], acc[x][y], 0, 0, 0);
   }
 
-  // lane l, block (x, y), value v: vocabulary row v0 + 64 wv + 32 x + 8(v/4)
-  // + 4 half + v%4, query row row0 + 64 wr + 32 y + col
-  unsigned long long best[2] = {0ull, 0ull};
+  // lane l, block (x, y), value v: vocabulary row v0 + 32 (XB wv + x) + 8(v/4)
+  // + 4 half + v%4, query row row0 + 32 (YB wr + y) + col
+  unsigned long long best[YB];
 #pragma unroll
-  for (int y = 0; y < 2; ++y) {
-    const int row = row0 + wr * 64 + y * 32 + col;
+  for (int y = 0; y < YB; ++y) {
+    best[y] = 0ull;
+    const int row = row0 + wr * YB * 32 + y * 32 + col;
     const bool row_ok = row < a.rows;
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int vb = v0 + wv * 64 + x * 32 + 4 * half;
+    for (int x = 0; x < XB; ++x) {
+      const int vb = v0 + wv * XB * 32 + x * 32 + 4 * half;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int vi = vb + 8 * (v >> 2) + (v & 3);
@@ -437,24 +484,32 @@ __global__ __launch_bounds__(512, 1) void lmhead_gemm_kernel(LmArgs a) {
   }
   wait_vmcnt<0>();                        // trailing zero-tile loads have landed
   lds_barrier();                          // every wavefront is done with the ring
-  unsigned long long* red = reinterpret_cast<unsigned long long*>(ring);   // [4 vocabulary groups][128 rows]
+  unsigned long long* red = reinterpret_cast<unsigned long long*>(ring);   // [NWV vocabulary groups][RB rows]
 #pragma unroll
-  for (int y = 0; y < 2; ++y) {
+  for (int y = 0; y < YB; ++y) {
     unsigned long long k = best[y];
     const auto lo = __builtin_amdgcn_permlane32_swap(uint32_t(k), uint32_t(k), false, false);
     const auto hi = __builtin_amdgcn_permlane32_swap(uint32_t(k >> 32), uint32_t(k >> 32), false, false);
     k = umax64((static_cast<unsigned long long>(hi[0]) << 32) | lo[0],
                (static_cast<unsigned long long>(hi[1]) << 32) | lo[1]);
-    if (half == 0) red[wv * G_RB + wr * 64 + y * 32 + col] = k;
+    if (half == 0) red[wv * C::RB + wr * YB * 32 + y * 32 + col] = k;
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): the LDS writes are done
   lds_barrier();
-  if (tid < G_RB && row0 + tid < a.rows) {
+  if (tid < C::RB && row0 + tid < a.rows) {
     unsigned long long k = red[tid];
 #pragma unroll
-    for (int g = 1; g < 4; ++g) k = umax64(k, red[g * G_RB + tid]);
+    for (int g = 1; g < NWV; ++g) k = umax64(k, red[g * C::RB + tid]);
     a.keys[size_t(row0 + tid) * a.nwg + vt] = k;
   }
+}
+
+__global__ __launch_bounds__(512, 1) void lmhead_gemm_kernel(LmArgs a) {
+  lmhead_gemm_body<GemmNarrow>(a);
+}
+
+__global__ __launch_bounds__(512, 1) void lmhead_gemm_wide_kernel(LmArgs a) {
+  lmhead_gemm_body<GemmWide>(a);
 }
 
 }  // namespace
@@ -465,7 +520,7 @@ hipError_t launch_lmhead(const LmHeadPlan& p, const void* hidden, const void* we
            static_cast<unsigned long long*>(ws), p.rows, p.hidden, p.V, p.nwg, p.nrc};
   if (p.gemm) {
     const dim3 grid(unsigned((int64_t(p.nwg) + 7) / 8 * 8 * p.nrc));
-    return launch_kernel(&lmhead_gemm_kernel, grid, dim3(512), stream, a);
+    return launch_kernel(p.gemm == 2 ? &lmhead_gemm_wide_kernel : &lmhead_gemm_kernel, grid, dim3(512), stream, a);
   }
   const dim3 grid(unsigned(int64_t(p.nwg) * p.nrc));
   if (p.hidden <= kLmRegHidden) return launch_kernel(&lmhead_rows_kernel, grid, dim3(512), stream, a);

@@ -114,14 +114,59 @@ def test_lmhead_accept_matches_oracle(lib, n_acc):
     assert np.all(na == n_acc)
 
 
-# more than 64 rows take the GEMM-tiled kernel (256 vocabulary x 128 row tiles)
-@pytest.mark.parametrize("R,Hd,V", [(65, 192, 300), (129, 256, 5000), (300, 1024, 20011), (200, 8192, 3000)])
+# more than 64 rows take a GEMM-tiled kernel: 256 vocabulary x 128 row tiles,
+# or 256 x 256 tiles where those fill rounds of 256 workgroups better.  Every
+# shape below has ragged row and vocabulary tails; 300 rows over 25523 words
+# (100 vocabulary tiles) take the wide kernel (200 workgroups against 300), the
+# others the narrow one; hidden 64 has fewer hidden tiles than either ring
+# has stages in flight.
+@pytest.mark.parametrize("R,Hd,V", [(65, 192, 300), (128, 320, 4099), (129, 256, 5000), (130, 64, 777),
+                                    (257, 128, 1000), (300, 1024, 20011), (200, 8192, 3000),
+                                    (300, 64, 25523), (300, 1024, 25523)])
 def test_gemm_tiled_planted_winner(lib, R, Hd, V):
     from synth import make_lmhead_case
     c = make_lmhead_case(R * 13 + V, R, Hd, V)
     tok, logits = run(lib, c)
     check_against_oracle(c, tok, logits, exact_tokens=True)
     assert np.array_equal(tok, c.targets)
+
+
+def _logits_of(lib, h, w, lo, hi):
+    out = torch.full((hi - lo,), -7, dtype=torch.int32, device="cuda")
+    lg = torch.full((hi - lo, w.shape[0]), float("nan"), dtype=torch.float32, device="cuda")
+    lib.orthrus_lmhead_argmax(h[lo:hi].contiguous(), w, out, logits=lg)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lg.cpu().numpy()
+
+
+def test_gemm_kernels_agree_bit_for_bit(lib):
+    """Both GEMM kernels keep one fp32 running sum per logit over the hidden
+    dimension in 16-element products taken in increasing order, so the wide
+    kernel (300 rows over 100 vocabulary tiles) and the narrow one (the same
+    rows in calls of 129 and 171) give identical logits and tokens."""
+    from synth import make_lmhead_case
+    c = make_lmhead_case(31, 300, 1024, 25523, plant=False)
+    tok_all, logits_all = run(lib, c)
+    check_against_oracle(c, tok_all, logits_all, exact_tokens=False)
+    h, w = bf16_dev(c.hidden), bf16_dev(c.weight)
+    for lo, hi in ((0, 129), (129, 300)):
+        tok, lg = _logits_of(lib, h, w, lo, hi)
+        assert np.array_equal(lg.view(np.uint32), logits_all[lo:hi].view(np.uint32)), (lo, hi)
+        assert np.array_equal(tok, tok_all[lo:hi]), (lo, hi)
+
+
+@pytest.mark.parametrize("Hd", [1024, 8192])
+def test_row_kernels_do_not_depend_on_the_other_rows(lib, Hd):
+    """Up to 64 rows, a row's logits are the same bits whatever rows share the
+    call (row-streaming kernel at hidden 1024, tile kernel at 8192)."""
+    from synth import make_lmhead_case
+    c = make_lmhead_case(37, 64, Hd, 3001, plant=False)
+    h, w = bf16_dev(c.hidden), bf16_dev(c.weight)
+    tok_all, lg_all = _logits_of(lib, h, w, 0, 64)
+    for lo, hi in ((0, 1), (5, 38), (63, 64)):
+        tok, lg = _logits_of(lib, h, w, lo, hi)
+        assert np.array_equal(lg.view(np.uint32), lg_all[lo:hi].view(np.uint32)), (lo, hi)
+        assert np.array_equal(tok, tok_all[lo:hi]), (lo, hi)
 
 
 def test_gemm_tiled_random_rows(lib):
