@@ -67,16 +67,17 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(key: str = "hbm_bytes_per_attention_call"):
+def measured_traffic(workload: str, key: str = "hbm_bytes_per_attention_call"):
     """HBM bytes per attention call (bf16 cache, or key
     "hbm_bytes_per_fp8_attention_call") from the committed rocprofv3 counter
-    summary, or None if the attention kernel changed since it was taken."""
+    summary, or None if it was taken on another workload or the attention
+    kernel changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("attn_source_sha256_16") != kernel_source_hash():
+    if t.get("attn_source_sha256_16") != kernel_source_hash() or t.get("workload") != workload:
         return None
     return t.get(key)
 
@@ -315,7 +316,7 @@ def main():
     dom = max(("draft_attn", "verify_attn"), key=lambda o: op_ms[o])
     dom_s = op_ms[dom] * 1e-3
     achieved = attn_bytes / dom_s / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic(args.workload)
 
     value = 2 * kv_bytes / (ms_per_step * 1e-3) / 1e9   # KV bytes of both passes per step
     res = {
@@ -364,7 +365,8 @@ def main():
                    "algorithmic_bytes_per_launch": lm_bytes}
     else:                # GEMM-tiled kernel: a dense contraction over B*K rows
         lm_flops = 2.0 * B * K * V * Hd
-        lm_roof = {"kernel": "lmhead_gemm_kernel + argmax_final_kernel (one ABI call)", "bound": "mfma",
+        lm_roof = {"kernel": "lmhead_gemm_kernel or lmhead_gemm_wide_kernel (the host's pick) + argmax_final_kernel"
+                             " (one ABI call)", "bound": "mfma",
                    "achieved": round(lm_flops / lm_s / 1e12, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                    "frac": round(lm_flops / lm_s / 1e12 / BF16_PEAK_TFLOPS, 4), "traffic": None,
                    "algorithmic_flops_per_launch": lm_flops, "algorithmic_bytes_per_launch": lm_bytes}
@@ -386,7 +388,7 @@ def main():
                      "bound": "hbm", "achieved": round(attn_bytes8 / (op_ms[dom8] * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_bytes8 / (op_ms[dom8] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic("hbm_bytes_per_fp8_attention_call"),
+                     "traffic": measured_traffic(args.workload, "hbm_bytes_per_fp8_attention_call"),
                      "algorithmic_bytes_per_launch": attn_bytes8,
                      "mfma_tflops": round(attn_flops / (op_ms[dom8] * 1e-3) / 1e12, 1)},
     }
