@@ -59,6 +59,9 @@ def parse_args():
     p.add_argument("--e2e", action="store_true",
                    help="only time whole decode steps of the Qwen3-8B-shaped model (greedy vs Orthrus)")
     p.add_argument("--e2e-contexts", default="4096,40960")
+    p.add_argument("--lmhead-rows", type=int, default=0,
+                   help="only time the fused LM head + argmax of the Qwen3-8B shape (hidden 4096, "
+                        "vocabulary 151936) over this many rows, eager launches (for profiler runs)")
     return p.parse_args()
 
 
@@ -96,6 +99,33 @@ def to_dev16(torch, np, a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+def lmhead_only(args, torch, dv, synth):
+    """The fused LM head + argmax alone at the Qwen3-8B shape over
+    args.lmhead_rows rows: weights N(0, 0.02) and hidden states N(0, 1), bf16,
+    drawn on the device; args.warmup untimed and args.steps timed eager calls."""
+    w = synth.WORKLOADS["qwen3_8b_40k"]
+    V, Hd, R = w["V"], w["hidden"], args.lmhead_rows
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(w["seed"] + 7)
+    lm_w = torch.randn((V, Hd), generator=gen, device=dev).mul_(0.02).to(torch.bfloat16)
+    lm_h = torch.randn((R, Hd), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty(R, dtype=torch.int32, device=dev)
+    ws = dv.lmhead_workspace(R, Hd, V, dev)
+    for _ in range(args.warmup):
+        dv.orthrus_lmhead_argmax(lm_h, lm_w, out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dv.orthrus_lmhead_argmax(lm_h, lm_w, out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / max(args.steps, 1) * 1e3
+    return {"lmhead_rows": R, "hidden": Hd, "vocab": V, "us_per_call": round(us, 1),
+            "tflops": round(2.0 * R * Hd * V / (us * 1e-6) / 1e12, 1),
+            "weight_gbps": round(V * Hd * 2 / (us * 1e-6) / 1e9, 1)}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -128,6 +158,10 @@ def main():
 
     if args.e2e:
         print(json.dumps(e2e(args, torch, dv, synth)), flush=True)
+        return
+
+    if args.lmhead_rows > 0:
+        print(json.dumps(lmhead_only(args, torch, dv, synth)), flush=True)
         return
 
     w, case, (qv, kbv, vbv), cons = setup(args, torch, dv, synth)
