@@ -61,6 +61,20 @@ int main() {
   EXPECT(check_accept(reinterpret_cast<const float*>(P), I, 1, 32, 1024, const_cast<int32_t*>(I), const_cast<int32_t*>(I), const_cast<int32_t*>(I), nullptr, P, 1 << 20, &ap, &err) == ORTHRUS_ERR_INVALID_ARG);
   EXPECT(check_accept(reinterpret_cast<const float*>(P), I, 1, 65, 1024, const_cast<int32_t*>(I), const_cast<int32_t*>(I), const_cast<int32_t*>(I), const_cast<int32_t*>(I), P, 1 << 20, &ap, &err) == ORTHRUS_ERR_UNSUPPORTED_SHAPE);
 
+  // LM head: rows kernel up to 64 rows; above, the GEMM tile whose workgroups
+  // fill rounds of 256 CUs better (wide tiles cost ~1.87x a narrow one)
+  LmHeadPlan lp;
+  EXPECT(plan_lmhead(32, 4096, 151936, &lp, nullptr) && lp.gemm == 0 && lp.nwg == 256 && lp.nrc == 1);
+  EXPECT(plan_lmhead(64, 4096, 151936, &lp, nullptr) && lp.gemm == 0 && lp.nrc == 2);
+  EXPECT(plan_lmhead(65, 4096, 151936, &lp, nullptr) && lp.gemm == 1 && lp.nwg == 594 && lp.nrc == 1);
+  EXPECT(plan_lmhead(128, 4096, 151936, &lp, nullptr) && lp.gemm == 1);
+  EXPECT(plan_lmhead(384, 4096, 151936, &lp, nullptr) && lp.gemm == 1 && lp.nrc == 3);
+  EXPECT(plan_lmhead(512, 4096, 151936, &lp, nullptr) && lp.gemm == 2 && lp.nwg == 594 && lp.nrc == 2);
+  EXPECT(lp.ws_bytes >= size_t(512) * 594 * 8);
+  EXPECT(plan_lmhead(300, 1024, 25523, &lp, nullptr) && lp.gemm == 2 && lp.nwg == 100 && lp.nrc == 2);
+  EXPECT(plan_lmhead(300, 1024, 20011, &lp, nullptr) && lp.gemm == 1);
+  EXPECT(!plan_lmhead(32, 4000, 151936, &lp, nullptr));   // hidden not a multiple of 64
+
   int32_t* O = reinterpret_cast<int32_t*>(uintptr_t(0x30000));
   const int64_t pool = int64_t(4096) * 8 * 16 * 128;
   EXPECT(check_commit(&kv, 2, pool, P, P, 32 * 8 * 128, I, 1, 32, O, &err) == ORTHRUS_OK);
