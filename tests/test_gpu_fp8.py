@@ -153,6 +153,33 @@ def test_qwen3_8b_40k_sharp(lib, mode):
     compare(run_fp8(lib, c, f, mode), oracle_fp8(c, f, mode), f"fp8 40k {mode}")
 
 
+def _random_shape(i):
+    """Seeded random e4m3-cache shape: batch 1-3, K 1-64, 1-4 KV heads, group
+    1-16, head_dim 128, cached lengths 0-1500 (ragged), a split size from the
+    library's choice down to one tile, and sometimes a max_ctx above the
+    longest sequence."""
+    rng = np.random.default_rng(3000 + i)
+    B = int(rng.integers(1, 4))
+    K = int(rng.choice([1, 2, 7, 8, 13, 32, 33, 64]))
+    Hkv = int(rng.integers(1, 5))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    lens = [int(x) for x in rng.integers(0, 1501, size=B)]
+    split = int(rng.choice([0, 64, 128, 320]))
+    slack = int(rng.choice([0, 0, 700]))
+    return B, K, G * Hkv, Hkv, lens, split, slack
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shapes(lib, i):
+    B, K, Hq, Hkv, lens, split, slack = _random_shape(i)
+    c = case(4000 + i, B, K, Hq, Hkv, lens, sharp=bool(i % 2), extra_pages_per_seq=(slack + 15) // 16)
+    f = to_fp8(c)
+    print(f"fp8 random {i}: B={B} K={K} Hq={Hq} Hkv={Hkv} lens={lens} split={split} slack={slack}", flush=True)
+    for mode in ("draft", "verify"):
+        got = run_fp8(lib, c, f, mode, max_ctx=max(lens) + slack, split=split)
+        compare(got, oracle_fp8(c, f, mode), f"fp8 random {i} {mode}")
+
+
 def test_k1_decode_and_last_row(lib):
     c = case(45, 2, 1, 32, 8, [777, 3000], sharp=True)
     f = to_fp8(c)
