@@ -399,7 +399,7 @@ def main():
                    "algorithmic_bytes_per_launch": lm_bytes}
     else:                # GEMM-tiled kernel: a dense contraction over B*K rows
         lm_flops = 2.0 * B * K * V * Hd
-        lm_roof = {"kernel": "lmhead_gemm_kernel or lmhead_gemm_wide_kernel (the host's pick) + argmax_final_kernel"
+        lm_roof = {"kernel": "lmhead_gemm_range_kernel, lmhead_gemm_kernel or lmhead_gemm_wide_kernel (the host's pick) + argmax_final_kernel"
                              " (one ABI call)", "bound": "mfma",
                    "achieved": round(lm_flops / lm_s / 1e12, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                    "frac": round(lm_flops / lm_s / 1e12 / BF16_PEAK_TFLOPS, 4), "traffic": None,

@@ -181,8 +181,13 @@ bool plan_lmhead(int rows, int hidden, int V, LmHeadPlan* p, std::string* why) {
     const int64_t narrow = ceil_div(V, kLmGemmVocabTile) * ceil_div(rows, kLmGemmRowTile);
     const int64_t wide = ceil_div(V, kLmGemmWideVocabTile) * ceil_div(rows, kLmGemmWideRowTile);
     p->gemm = ceil_div(wide, 256) * 187 < ceil_div(narrow, 256) * 100 ? 2 : 1;
+    // one row tile: contiguous vocabulary ranges, one workgroup per CU
+    if (p->gemm == 1 && rows <= kLmGemmRowTile) p->gemm = 3;
   }
-  if (p->gemm == 2) {
+  if (p->gemm == 3) {
+    p->nwg = V < kLmWorkgroups ? V : kLmWorkgroups;
+    p->nrc = 1;
+  } else if (p->gemm == 2) {
     p->nwg = int(ceil_div(V, kLmGemmWideVocabTile));
     p->nrc = int(ceil_div(rows, kLmGemmWideRowTile));
   } else if (p->gemm == 1) {

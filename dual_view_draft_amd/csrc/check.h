@@ -49,7 +49,7 @@ constexpr int kLmGemmWideRowTile = 256;
 
 struct LmHeadPlan {
   int rows = 0, hidden = 0, V = 0;
-  int gemm = 0;          // 0: rows kernel; 1: GEMM 256 x 128 tiles; 2: GEMM 256 x 256 tiles
+  int gemm = 0;          // 0: rows kernel; GEMM: 1 256 x 128 tiles, 2 256 x 256 tiles, 3 vocabulary ranges
   int nwg = 0;           // vocabulary ranges (or tiles) = argmax key chunks per row
   int nrc = 0;           // row chunks of kLmRowChunk rows (or row tiles)
   size_t ws_bytes = 0;   // keys [rows][nwg] (8 bytes each)

@@ -344,11 +344,11 @@ __global__ __launch_bounds__(512, 1) void lmhead_rows_kernel(LmArgs a) {
 //   four 32 KiB stages.  It loads 1.5 times fewer bytes into LDS per product
 //   and reads 6 operand blocks from LDS per 8 products instead of 4 per 4,
 //   which makes a workgroup about 7 % cheaper per product.
-// The host takes the one whose workgroups fill rounds of 256 CUs better.
-// With a single row tile (at most 128 rows) no two workgroups read the same
-// weights, so the narrow kernel then streams them with the non-temporal
-// policy (8 % faster at 96-128 rows); otherwise the default policy keeps them
-// in L2 for the other row tiles (the non-temporal policy cost 10 % there).
+// The host takes the one whose workgroups fill rounds of 256 CUs better;
+// with a single row tile (at most 128 rows) it takes the narrow kernel's
+// range mode (below).  Where several row tiles read the same weights, they
+// keep the default cache policy, which leaves them in L2 for the other row
+// tiles (the non-temporal policy cost 10 % at 512 and 768 rows).
 // Both keep one fp32 running sum per logit over 16-element products in
 // increasing hidden order, so they agree bit for bit.  The row-streaming
 // kernel instead adds eight per-wavefront partial sums, so a row's logits
@@ -378,49 +378,78 @@ using GemmWide = GemmCfg<2, 4, 4, 2, 32, 4>;
 static_assert(GemmNarrow::VB == kLmGemmVocabTile && GemmNarrow::RB == kLmGemmRowTile &&
               GemmWide::VB == kLmGemmWideVocabTile && GemmWide::RB == kLmGemmWideRowTile, "host tiles");
 
-// NT: the weights take the non-temporal policy (one row tile: no other
-// workgroup reads them).
-template <class C, bool NT>
+// RANGE (a single row tile, at most RB rows): workgroup wg takes the
+// contiguous vocabulary range [V wg / nwg, V (wg + 1) / nwg) (nwg = 256, one
+// per CU) and runs its blocks of VB rows back to back through the same ring,
+// so the work is not cut into whole tiles that fill the CUs unevenly; no
+// other workgroup reads its weights, so they take the non-temporal policy.
+// Otherwise each workgroup owns one VB x RB output tile.
+template <class C, bool RANGE>
 __device__ __forceinline__ void lmhead_gemm_body(const LmArgs& a) {
   constexpr int NWV = C::NWV, NWR = C::NWR, XB = C::XB, YB = C::YB, GKT = C::GKT, GNS = C::GNS;
   __shared__ __attribute__((aligned(16))) uint16_t ring[GNS * C::STAGE];
-  // workgroup -> (vocabulary tile, row tile); the grid is padded to a
-  // multiple of 8 vocabulary tiles
-  const int L = blockIdx.x;
-  const int m = L >> 3;
-  const int vt = (m / a.nrc) * 8 + (L & 7);
-  const int rt = m - (m / a.nrc) * a.nrc;
-  if (vt >= a.nwg) return;                       // uniform: padding
-  const int v0 = vt * C::VB, row0 = rt * C::RB;
+  int slot, v0, v1, row0;                        // key slot, vocabulary range, first query row
+  if constexpr (RANGE) {
+    slot = blockIdx.x;
+    v0 = int((int64_t(a.V) * slot) / a.nwg);
+    v1 = int((int64_t(a.V) * (slot + 1)) / a.nwg);
+    row0 = 0;
+  } else {
+    // workgroup -> (vocabulary tile, row tile); the grid is padded to a
+    // multiple of 8 vocabulary tiles
+    const int L = blockIdx.x;
+    const int m = L >> 3;
+    slot = (m / a.nrc) * 8 + (L & 7);
+    const int rt = m - (m / a.nrc) * a.nrc;
+    if (slot >= a.nwg) return;                   // uniform: padding
+    v0 = slot * C::VB;
+    v1 = min(v0 + C::VB, a.V);
+    row0 = rt * C::RB;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, col = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wv = wave % NWV, wr = wave / NWV;
   const int nkt = a.hidden / GKT;
+  const int nblk = RANGE ? (v1 - v0 + C::VB - 1) / C::VB : 1;
+  const int ntiles = RANGE ? nblk * nkt : nkt;   // (vocabulary block, hidden tile) pairs, block-major
 
-  // Loads of hidden tile kt into stage st: wavefront w fills the 1 KiB
-  // chunks w + 8i of the stage (weight rows first, then query rows), lane l
-  // row RPL c + l / GR and granule l % GR of the LDS row, which holds logical
-  // granule (l % GR) ^ swz(row).  Rows outside the vocabulary or past the
-  // last query row, and tiles past the end, load the 16 zero bytes, so every
-  // step issues LPT loads.
+  // Loads of tile t into stage st (tiles are issued in order; in a range,
+  // tile t is block ib, hidden tile ik): wavefront w fills the 1 KiB chunks
+  // w + 8i of the stage (weight rows first, then query rows), lane l row
+  // RPL c + l / GR and granule l % GR of the LDS row, which holds logical
+  // granule (l % GR) ^ swz(row).  Rows outside the range or past the last
+  // query row, and tiles past the end, load the 16 zero bytes, so every step
+  // issues LPT loads.
   const int lr = lane / C::GR, lp = lane % C::GR;
-  auto issue_tile = [&](int kt, uint16_t* st) {
-    const bool live = kt < nkt;
+  int ib = 0, ik = 0;
+  auto issue_tile = [&](int t, uint16_t* st) {
+    bool live;
+    int blk, kt;
+    if constexpr (RANGE) {
+      live = ib < nblk;
+      blk = ib;
+      kt = ik;
+      if (++ik == nkt) { ik = 0; ++ib; }
+    } else {
+      live = t < nkt;
+      blk = 0;
+      kt = t;
+    }
 #pragma unroll
     for (int i = 0; i < C::LPT; ++i) {
       const int c = wave + 8 * i;
       const void* src = g_lm_zero16;
       if (i < C::WLPT) {
         const int r = c * C::RPL + lr;
-        const int v = v0 + r;
-        if (live && v < a.V) src = a.w + size_t(v) * a.hidden + kt * GKT + (lp ^ C::swz(r)) * 8;
+        const int v = v0 + blk * C::VB + r;
+        if (live && v < v1) src = a.w + size_t(v) * a.hidden + kt * GKT + (lp ^ C::swz(r)) * 8;
       } else {
         const int r = (c - C::WCH) * C::RPL + lr;
         const int hr = row0 + r;
         if (live && hr < a.rows) src = a.h + size_t(hr) * a.hidden + kt * GKT + (lp ^ C::swz(r)) * 8;
       }
-      if (NT && i < C::WLPT) load_lds16<true>(src, lds_addr(st + c * C::RPL * GKT));   // i: unrolled constant
+      if (RANGE && i < C::WLPT) load_lds16<true>(src, lds_addr(st + c * C::RPL * GKT));   // i: unrolled constant
       else load_lds16(src, lds_addr(st + c * C::RPL * GKT));
     }
   };
@@ -432,12 +461,40 @@ __device__ __forceinline__ void lmhead_gemm_body(const LmArgs& a) {
   for (int x = 0; x < XB; ++x)
 #pragma unroll
     for (int y = 0; y < YB; ++y) acc[x][y] = f32x16{};
-  for (int kt = 0; kt < nkt; ++kt) {
-    wait_vmcnt<(GNS - 2) * C::LPT>();    // tile kt has landed for this wavefront
-    lds_barrier();                       // ... for every wavefront; stage of kt-1 is free
-    const int tn = kt + GNS - 1;
+  unsigned long long best[YB];                   // best key of each of this lane's query rows
+#pragma unroll
+  for (int y = 0; y < YB; ++y) best[y] = 0ull;
+  // Keys (and, on request, logits) of vocabulary block blk once its sums are
+  // complete; the accumulators restart at zero.  Lane l, block (x, y), value
+  // v: vocabulary row v0 + VB blk + 32 (XB wv + x) + 8(v/4) + 4 half + v%4,
+  // query row row0 + 32 (YB wr + y) + col.
+  auto block_keys = [&](int blk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int y = 0; y < YB; ++y) {
+      const int row = row0 + wr * YB * 32 + y * 32 + col;
+      const bool row_ok = row < a.rows;
+#pragma unroll
+      for (int x = 0; x < XB; ++x) {
+        const int vb = v0 + blk * C::VB + wv * XB * 32 + x * 32 + 4 * half;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int vi = vb + 8 * (v >> 2) + (v & 3);
+          if (vi < v1) {
+            best[y] = umax64(best[y], make_key(acc[x][y][v], vi));
+            if (a.logits && row_ok) a.logits[size_t(row) * a.V + vi] = acc[x][y][v];
+          }
+        }
+        acc[x][y] = f32x16{};
+      }
+    }
+  };
+  int cb = 0, ck = 0;                            // block and hidden tile of the tile being computed
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmcnt<(GNS - 2) * C::LPT>();    // tile t has landed for this wavefront
+    lds_barrier();                       // ... for every wavefront; stage of t-1 is free
+    const int tn = t + GNS - 1;
     issue_tile(tn, ring + (tn % GNS) * C::STAGE);
-    const uint16_t* wt = ring + (kt % GNS) * C::STAGE;
+    const uint16_t* wt = ring + (t % GNS) * C::STAGE;
     const uint16_t* ht = wt + C::W;
     // All operand reads of the tile go out first, so their LDS latency is
     // paid once per tile rather than once per k-step (the scheduling barrier
@@ -466,29 +523,17 @@ __device__ __forceinline__ void lmhead_gemm_body(const LmArgs& a) {
 #pragma unroll
         for (int y = 0; y < YB; ++y)
           acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks][x], bv[ks][y], acc[x][y], 0, 0, 0);
-  }
 
-  // lane l, block (x, y), value v: vocabulary row v0 + 32 (XB wv + x) + 8(v/4)
-  // + 4 half + v%4, query row row0 + 32 (YB wr + y) + col
-  unsigned long long best[YB];
-#pragma unroll
-  for (int y = 0; y < YB; ++y) {
-    best[y] = 0ull;
-    const int row = row0 + wr * YB * 32 + y * 32 + col;
-    const bool row_ok = row < a.rows;
-#pragma unroll
-    for (int x = 0; x < XB; ++x) {
-      const int vb = v0 + wv * XB * 32 + x * 32 + 4 * half;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int vi = vb + 8 * (v >> 2) + (v & 3);
-        if (vi < a.V) {
-          best[y] = umax64(best[y], make_key(acc[x][y][v], vi));
-          if (a.logits && row_ok) a.logits[size_t(row) * a.V + vi] = acc[x][y][v];
-        }
+    if constexpr (RANGE) {
+      if (++ck == nkt) {                 // uniform: block cb's logits are complete
+        block_keys(cb);
+        ck = 0;
+        ++cb;
       }
     }
   }
+  if constexpr (!RANGE) block_keys(0);
+
   wait_vmcnt<0>();                        // trailing zero-tile loads have landed
   lds_barrier();                          // every wavefront is done with the ring
   unsigned long long* red = reinterpret_cast<unsigned long long*>(ring);   // [NWV vocabulary groups][RB rows]
@@ -507,13 +552,16 @@ __device__ __forceinline__ void lmhead_gemm_body(const LmArgs& a) {
     unsigned long long k = red[tid];
 #pragma unroll
     for (int g = 1; g < NWV; ++g) k = umax64(k, red[g * C::RB + tid]);
-    a.keys[size_t(row0 + tid) * a.nwg + vt] = k;
+    a.keys[size_t(row0 + tid) * a.nwg + slot] = k;
   }
 }
 
-template <bool NT>
 __global__ __launch_bounds__(512, 1) void lmhead_gemm_kernel(LmArgs a) {
-  lmhead_gemm_body<GemmNarrow, NT>(a);
+  lmhead_gemm_body<GemmNarrow, false>(a);
+}
+
+__global__ __launch_bounds__(512, 1) void lmhead_gemm_range_kernel(LmArgs a) {
+  lmhead_gemm_body<GemmNarrow, true>(a);
 }
 
 __global__ __launch_bounds__(512, 1) void lmhead_gemm_wide_kernel(LmArgs a) {
@@ -529,9 +577,8 @@ hipError_t launch_lmhead(const LmHeadPlan& p, const void* hidden, const void* we
   if (p.gemm) {
     const dim3 grid(unsigned((int64_t(p.nwg) + 7) / 8 * 8 * p.nrc));
     if (p.gemm == 2) return launch_kernel(&lmhead_gemm_wide_kernel, grid, dim3(512), stream, a);
-    // a single row tile reads every weight once
-    if (p.nrc == 1) return launch_kernel(&lmhead_gemm_kernel<true>, grid, dim3(512), stream, a);
-    return launch_kernel(&lmhead_gemm_kernel<false>, grid, dim3(512), stream, a);
+    if (p.gemm == 3) return launch_kernel(&lmhead_gemm_range_kernel, dim3(p.nwg), dim3(512), stream, a);
+    return launch_kernel(&lmhead_gemm_kernel, grid, dim3(512), stream, a);
   }
   const dim3 grid(unsigned(int64_t(p.nwg) * p.nrc));
   if (p.hidden <= kLmRegHidden) return launch_kernel(&lmhead_rows_kernel, grid, dim3(512), stream, a);

@@ -61,13 +61,17 @@ int main() {
   EXPECT(check_accept(reinterpret_cast<const float*>(P), I, 1, 32, 1024, const_cast<int32_t*>(I), const_cast<int32_t*>(I), const_cast<int32_t*>(I), nullptr, P, 1 << 20, &ap, &err) == ORTHRUS_ERR_INVALID_ARG);
   EXPECT(check_accept(reinterpret_cast<const float*>(P), I, 1, 65, 1024, const_cast<int32_t*>(I), const_cast<int32_t*>(I), const_cast<int32_t*>(I), const_cast<int32_t*>(I), P, 1 << 20, &ap, &err) == ORTHRUS_ERR_UNSUPPORTED_SHAPE);
 
-  // LM head: rows kernel up to 64 rows; above, the GEMM tile whose workgroups
+  // LM head: rows kernel up to 64 rows; one row tile (up to 128 rows): GEMM
+  // over contiguous vocabulary ranges; above, the GEMM tile whose workgroups
   // fill rounds of 256 CUs better (wide tiles cost ~1.87x a narrow one)
   LmHeadPlan lp;
   EXPECT(plan_lmhead(32, 4096, 151936, &lp, nullptr) && lp.gemm == 0 && lp.nwg == 256 && lp.nrc == 1);
   EXPECT(plan_lmhead(64, 4096, 151936, &lp, nullptr) && lp.gemm == 0 && lp.nrc == 2);
-  EXPECT(plan_lmhead(65, 4096, 151936, &lp, nullptr) && lp.gemm == 1 && lp.nwg == 594 && lp.nrc == 1);
-  EXPECT(plan_lmhead(128, 4096, 151936, &lp, nullptr) && lp.gemm == 1);
+  EXPECT(plan_lmhead(65, 4096, 151936, &lp, nullptr) && lp.gemm == 3 && lp.nwg == 256 && lp.nrc == 1);
+  EXPECT(plan_lmhead(128, 4096, 151936, &lp, nullptr) && lp.gemm == 3);
+  EXPECT(plan_lmhead(100, 192, 300, &lp, nullptr) && lp.gemm == 3 && lp.nwg == 256);
+  EXPECT(plan_lmhead(100, 192, 77, &lp, nullptr) && lp.gemm == 3 && lp.nwg == 77);
+  EXPECT(plan_lmhead(129, 4096, 151936, &lp, nullptr) && lp.gemm == 1 && lp.nwg == 594 && lp.nrc == 2);
   EXPECT(plan_lmhead(384, 4096, 151936, &lp, nullptr) && lp.gemm == 1 && lp.nrc == 3);
   EXPECT(plan_lmhead(512, 4096, 151936, &lp, nullptr) && lp.gemm == 2 && lp.nwg == 594 && lp.nrc == 2);
   EXPECT(lp.ws_bytes >= size_t(512) * 594 * 8);
