@@ -267,7 +267,7 @@ bool plan_sample(int stat_rows, int B, int V, SamplePlan* p) {
   // about 2048 workgroups over the statistics, 4096..16384 values per chunk
   int64_t chunk = round_up(ceil_div(int64_t(V) * (stat_rows > 0 ? stat_rows : 1), 2048), 1024);
   if (chunk < 4096) chunk = 4096;
-  if (chunk > 16384) chunk = 16384;
+  if (chunk > kSampleMaxChunk) chunk = kSampleMaxChunk;
   if (chunk > V) chunk = V;
   p->chunk = int(chunk);
   p->nchunks = int(ceil_div(V, chunk));

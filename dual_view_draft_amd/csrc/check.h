@@ -97,6 +97,7 @@ int check_commit(const orthrus_kv* kv, int layers, int64_t pool_layer_stride, co
 constexpr int kSampleSeqBytes = 32;
 constexpr int kSampleRowBytes = 16;
 constexpr int kResidualChunk = 1024;   // entries per residual chunk
+constexpr int kSampleMaxChunk = 16384; // entries per statistics chunk at most
 
 struct SamplePlan {
   int rows = 0;          // rows with chunk statistics

@@ -241,16 +241,27 @@ __device__ int draw(ChunkW chunk_w, Weight weight, int nchunks, int chunk, int V
 
 // Chunk statistics of every row: m_c and s_c = sum exp((z - m_c) / T).
 __global__ __launch_bounds__(kThreads) void sample_stats_kernel(StatsArgs a) {
+  constexpr int PER = kSampleMaxChunk / kThreads;   // entries per thread at most
   __shared__ float redf[4];
   __shared__ double redd[4];
   const int row = blockIdx.y, c = blockIdx.x;
   const float* z = row < a.rows0 ? a.z0 + size_t(row) * a.V : a.z1 + size_t(row - a.rows0) * a.V;
   const int v0 = c * a.chunk, v1 = min(v0 + a.chunk, a.V);
+  // thread t's entries v0 + t + 256 j, all loaded at once and kept in registers
+  float x[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int v = v0 + threadIdx.x + j * kThreads;
+    x[j] = v < v1 ? z[v] : -INFINITY;
+  }
   float m = -INFINITY;
-  for (int v = v0 + threadIdx.x; v < v1; v += kThreads) m = fmaxf(m, z[v]);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) m = fmaxf(m, x[j]);
   m = block_max(m, redf);
-  double s = 0.0;
-  for (int v = v0 + threadIdx.x; v < v1; v += kThreads) s += wexp(z[v], m, a.inv_t);
+  double s = 0.0;                                  // in increasing v, as the entries were read
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (v0 + int(threadIdx.x) + j * kThreads < v1) s += wexp(x[j], m, a.inv_t);
   s = block_sum(s, redd);
   if (threadIdx.x == 0) {
     a.cm[size_t(row) * a.nchunks + c] = m;
