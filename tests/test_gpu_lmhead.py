@@ -114,15 +114,16 @@ def test_lmhead_accept_matches_oracle(lib, n_acc):
     assert np.all(na == n_acc)
 
 
-# more than 64 rows take a GEMM-tiled kernel: 256 vocabulary x 128 row tiles,
-# or 256 x 256 tiles where those fill rounds of 256 workgroups better.  Every
-# shape below has ragged row and vocabulary tails; 300 rows over 25523 words
-# (100 vocabulary tiles) take the wide kernel (200 workgroups against 300), the
-# others the narrow one; hidden 64 has fewer hidden tiles than either ring
-# has stages in flight.
+# more than 64 rows take a GEMM-tiled kernel: up to 128 rows (one row tile)
+# the narrow kernel over contiguous vocabulary ranges (one per CU; 65 rows over
+# 300 words leaves most ranges one or two words long), above that 256 x 128
+# tiles, or 256 x 256 tiles where those fill rounds of 256 workgroups better.
+# Every shape below has ragged row and vocabulary tails; 300 rows over 25523
+# words (100 vocabulary tiles) take the wide kernel (200 workgroups against
+# 300); hidden 64 has fewer hidden tiles than either ring has stages in flight.
 @pytest.mark.parametrize("R,Hd,V", [(65, 192, 300), (128, 320, 4099), (129, 256, 5000), (130, 64, 777),
                                     (257, 128, 1000), (300, 1024, 20011), (200, 8192, 3000),
-                                    (300, 64, 25523), (300, 1024, 25523)])
+                                    (300, 64, 25523), (300, 1024, 25523), (96, 4096, 151936)])
 def test_gemm_tiled_planted_winner(lib, R, Hd, V):
     from synth import make_lmhead_case
     c = make_lmhead_case(R * 13 + V, R, Hd, V)
