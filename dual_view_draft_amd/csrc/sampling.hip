@@ -305,6 +305,47 @@ __global__ __launch_bounds__(kDrawThreads) void sample_draw_kernel(SampleArgs a)
   if (threadIdx.x == 0) a.out[row] = tok;
 }
 
+// Draw with the row's normalisation done in the same workgroup: wavefront 0
+// forms M, the chunk weights and Z exactly as row_norm_kernel does (the same
+// lane-strided order and butterfly), into LDS; then the draw as in
+// sample_draw_kernel.  One launch fewer for orthrus_sample, whose rows need
+// no normaliser afterwards.
+constexpr int kFusedMaxChunks = 1024;
+
+struct NormDrawArgs {
+  const float* z;
+  const float* u;      // [rows]
+  const float* cm;     // [rows][nchunks]
+  const double* cs;
+  int32_t* out;        // [rows]
+  int V, chunk, nchunks;
+  double inv_t;
+};
+
+__global__ __launch_bounds__(kDrawThreads) void sample_norm_draw_kernel(NormDrawArgs a) {
+  __shared__ double cw_s[kFusedMaxChunks];
+  __shared__ float m_s;
+  const int row = blockIdx.x;
+  if (threadIdx.x < 64) {                          // wavefront 0: row_norm_kernel's steps
+    const int lane = threadIdx.x;
+    const float* cm = a.cm + size_t(row) * a.nchunks;
+    const double* cs = a.cs + size_t(row) * a.nchunks;
+    float m = -INFINITY;
+    for (int c = lane; c < a.nchunks; c += 64) m = fmaxf(m, cm[c]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    for (int c = lane; c < a.nchunks; c += 64) cw_s[c] = cs[c] * wexp(cm[c], m, a.inv_t);
+    if (lane == 0) m_s = m;
+  }
+  __syncthreads();
+  const float M = m_s;
+  const float* z = a.z + size_t(row) * a.V;
+  const double inv_t = a.inv_t;
+  const int tok = draw([&](int c) { return cw_s[c]; }, [&](int v) { return wexp(z[v], M, inv_t); },
+                       a.nchunks, a.chunk, a.V, double(a.u[row]));
+  if (threadIdx.x == 0) a.out[row] = tok;
+}
+
 // One wavefront per sequence, lane i = block row i: the acceptance test of
 // every row, then the first rejection.
 __global__ __launch_bounds__(64) void sample_decide_kernel(DecideArgs a) {
@@ -439,6 +480,13 @@ hipError_t launch_sample(const SamplePlan& p, const float* logits, float tempera
                          int32_t* out, void* ws, hipStream_t stream) {
   const Ws w = carve(p, ws);
   const double inv_t = 1.0 / double(temperature);
+  if (p.nchunks <= kFusedMaxChunks) {
+    StatsArgs s{logits, logits, w.cm, w.cs, p.rows, p.rows, p.V, p.chunk, p.nchunks, inv_t};
+    hipError_t e = launch_kernel(&sample_stats_kernel, dim3(p.nchunks, p.rows), dim3(kThreads), stream, s);
+    if (e != hipSuccess) return e;
+    NormDrawArgs d{logits, u, w.cm, w.cs, out, p.V, p.chunk, p.nchunks, inv_t};
+    return launch_kernel(&sample_norm_draw_kernel, dim3(p.rows), dim3(kDrawThreads), stream, d);
+  }
   hipError_t e = launch_stats(p, w, logits, logits, p.rows, inv_t, stream);
   if (e != hipSuccess) return e;
   SampleArgs d{logits, u, w.cw, w.rn, out, p.V, p.chunk, p.nchunks, inv_t};
