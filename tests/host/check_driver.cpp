@@ -79,6 +79,13 @@ int main() {
   EXPECT(plan_lmhead(300, 1024, 20011, &lp, nullptr) && lp.gemm == 1);
   EXPECT(!plan_lmhead(32, 4000, 151936, &lp, nullptr));   // hidden not a multiple of 64
 
+  // sampling statistics: chunks of 4096..16384 entries; 1 x 4.2 M words makes
+  // 1026 chunks (more than the fused draw's 1024)
+  SamplePlan sp;
+  EXPECT(plan_sample(32, 0, 151936, &sp) && sp.chunk == 4096 && sp.nchunks == 38);
+  EXPECT(plan_sample(1, 0, 4200000, &sp) && sp.chunk == 4096 && sp.nchunks == 1026);
+  EXPECT(plan_sample(2, 0, 4200000, &sp) && sp.chunk <= kSampleMaxChunk && sp.nchunks <= 1024);
+
   int32_t* O = reinterpret_cast<int32_t*>(uintptr_t(0x30000));
   const int64_t pool = int64_t(4096) * 8 * 16 * 128;
   EXPECT(check_commit(&kv, 2, pool, P, P, 32 * 8 * 128, I, 1, 32, O, &err) == ORTHRUS_OK);
