@@ -139,6 +139,7 @@ int check_argmax(const float* logits, int rows, int V, const int32_t* out, const
                  size_t ws_bytes, ArgmaxPlan* plan, std::string* err) {
   if (rows < 0 || V < 1) return fail(err, ORTHRUS_ERR_INVALID_ARG, "rows must be >= 0 and vocab >= 1");
   if (rows > 65535) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "at most 65535 rows per call");
+  if (V > kMaxVocab) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "vocab must be <= 2^30");
   plan_argmax(rows, V, plan);
   if (rows == 0) return ORTHRUS_OK;
   if (!logits || !out) return fail(err, ORTHRUS_ERR_INVALID_ARG, "null logits/out");
@@ -168,6 +169,7 @@ bool plan_lmhead(int rows, int hidden, int V, LmHeadPlan* p, std::string* why) {
   auto no = [&](const char* m) { if (why) *why = m; return false; };
   if (rows < 0) return no("rows must be >= 0");
   if (V < 1) return no("vocab must be >= 1");
+  if (V > kMaxVocab) return no("vocab must be <= 2^30");
   if (hidden < kLmKTile || hidden % kLmKTile || hidden > (1 << 20))
     return no("hidden must be a multiple of 64 in [64, 2^20]");
   if (int64_t(rows) * V > (int64_t(1) << 40)) return no("rows * vocab too large");
@@ -289,6 +291,7 @@ int check_sample(const float* logits, int rows, int V, float temperature, const 
                  const void* ws, size_t ws_bytes, SamplePlan* plan, std::string* err) {
   if (rows < 0 || V < 1) return fail(err, ORTHRUS_ERR_INVALID_ARG, "rows must be >= 0 and vocab >= 1");
   if (rows > 65535) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "at most 65535 rows per call");
+  if (V > kMaxVocab) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "vocab must be <= 2^30");
   if (!(std::isfinite(temperature) && temperature > 0.f))
     return fail(err, ORTHRUS_ERR_INVALID_ARG, "temperature must be finite and > 0");
   plan_sample(rows, 0, V, plan);
@@ -308,6 +311,7 @@ int check_accept_sampled(const float* logits_d, const float* logits_a, const int
   if (B < 0) return fail(err, ORTHRUS_ERR_INVALID_ARG, "batch must be >= 0");
   if (K < 1 || K > ORTHRUS_MAX_BLOCK) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "block_k must be in [1, 64]");
   if (V < 1) return fail(err, ORTHRUS_ERR_INVALID_ARG, "vocab must be >= 1");
+  if (V > kMaxVocab) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "vocab must be <= 2^30");
   if (int64_t(B) * K * 2 > 65535) return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "2 * batch * block_k must be <= 65535");
   if (!(std::isfinite(temperature) && temperature > 0.f))
     return fail(err, ORTHRUS_ERR_INVALID_ARG, "temperature must be finite and > 0");

@@ -16,6 +16,9 @@ constexpr int kRowsPerWave = 32;   // query rows per wavefront (one 32x32 MFMA b
 constexpr int kMaxRowsPerCta = 128;
 constexpr int kMaxGroup = 16;
 constexpr int kMaxSplitTiles = 64;  // a context split covers at most 64 tiles (4096 tokens)
+// Largest vocabulary: chunk bounds (start + chunk length) stay below 2^31 in
+// the kernels' int32 index arithmetic.
+constexpr int kMaxVocab = 1 << 30;
 
 // Geometry of one attention call, all derived on the host.
 struct AttnPlan {

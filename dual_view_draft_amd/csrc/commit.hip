@@ -39,7 +39,9 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
   const int r = blockIdx.x;
   const int b = blockIdx.y;
   const int layer = blockIdx.z;
-  const int L = max(a.seq_lens[b], 0);
+  // A length beyond what the block table can address is clamped first, so
+  // L + r stays far below 2^31.
+  const int L = int(min(int64_t(max(a.seq_lens[b], 0)), int64_t(a.maxp) * ORTHRUS_PAGE_SIZE));
   int e = a.n_emit[b];
   e = e < 0 ? 0 : (e > a.K ? a.K : e);
   if (r == 0 && layer == 0 && threadIdx.x == 0) a.seq_lens_out[b] = L + e;

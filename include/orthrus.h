@@ -199,7 +199,7 @@ ORTHRUS_API size_t orthrus_argmax_workspace_bytes(int rows, int vocab);
  * draft logits (section 2.3 step 1).
  *  logits : fp32 [rows][vocab], finite (NaN is outside the contract)
  *  out    : int32 [rows]
- * 0 <= rows <= 65535 (0 = no-op), 1 <= vocab < 2^31.
+ * 0 <= rows <= 65535 (0 = no-op), 1 <= vocab <= 2^30.
  */
 ORTHRUS_API int orthrus_argmax(const float* logits, int rows, int vocab, int32_t* out,
                    void* workspace, size_t workspace_bytes, void* stream);
@@ -239,7 +239,7 @@ ORTHRUS_API int orthrus_accept(const float* logits_a, const int32_t* draft, int 
  *                  and for callers that need them)
  *  workspace     : >= orthrus_lmhead_workspace_bytes(rows, hidden, vocab)
  *                  bytes, 16-byte aligned; contents on entry do not matter.
- * Requirements: hidden a multiple of 64 in [64, 2^20]; 1 <= vocab < 2^31;
+ * Requirements: hidden a multiple of 64 in [64, 2^20]; 1 <= vocab <= 2^30;
  * 0 <= rows <= 65535 * 32 (0 = no-op).  The weights are read once per 32
  * rows (rows beyond 32 re-read them).  NaN logits are outside the contract.
  */
@@ -303,7 +303,7 @@ ORTHRUS_API size_t orthrus_sample_workspace_bytes(int rows, int vocab);
  *  logits : fp32 [rows][vocab], finite
  *  u      : fp32 [rows], each in [0, 1)
  *  out    : int32 [rows] (written)
- * 0 <= rows <= 65535 (0 = no-op); temperature finite and > 0.
+ * 0 <= rows <= 65535 (0 = no-op); 1 <= vocab <= 2^30; temperature finite and > 0.
  */
 ORTHRUS_API int orthrus_sample(const float* logits, int rows, int vocab, float temperature, const float* u,
                    int32_t* out, void* workspace, size_t workspace_bytes, void* stream);
@@ -326,7 +326,9 @@ ORTHRUS_API size_t orthrus_accept_sampled_workspace_bytes(int batch, int block_k
  *  tokens             : int32 [batch][block_k] (written) emitted tokens in
  *                       [0, n_emit), -1 after
  *  n_acc, n_emit, next_anchor : int32 [batch] (written), as in orthrus_accept
- * 1 <= block_k <= 64; 2 * batch * block_k <= 65535; temperature finite, > 0.
+ * 1 <= block_k <= 64; 2 * batch * block_k <= 65535; 1 <= vocab <= 2^30;
+ * temperature finite, > 0.  A drafted token outside [0, vocab) counts as
+ * probability 0 in both views (always rejected).
  */
 ORTHRUS_API int orthrus_accept_sampled(const float* logits_d, const float* logits_a, const int32_t* draft,
                            int batch, int block_k, int vocab, float temperature, const float* u_acc,

@@ -53,11 +53,17 @@ int main() {
   EXPECT(check_attention(&kv, nullptr, nullptr, nullptr, nullptr, 0, 32, 32, 0.1f, 100, 0, nullptr, 0, &plan, &err) == ORTHRUS_OK);
 
   ArgmaxPlan ap;
+  LmHeadPlan lp0;
   EXPECT(plan_argmax(32, 151936, &ap) && ap.chunk % 4 == 0 && int64_t(ap.chunk) * ap.nchunks >= 151936);
   EXPECT(check_argmax(reinterpret_cast<const float*>(P), 32, 151936, I, P, ap.ws_bytes, &ap, &err) == ORTHRUS_OK);
   EXPECT(check_argmax(reinterpret_cast<const float*>(P), 32, 151936, I, P, 8, &ap, &err) == ORTHRUS_ERR_WORKSPACE_TOO_SMALL);
   EXPECT(check_argmax(reinterpret_cast<const float*>(P), 32, 0, I, P, 1 << 20, &ap, &err) == ORTHRUS_ERR_INVALID_ARG);
   EXPECT(check_argmax(nullptr, 0, 10, nullptr, nullptr, 0, &ap, &err) == ORTHRUS_OK);
+  // vocabularies up to 2^30 keep every chunk bound (start + chunk) below 2^31
+  EXPECT(check_argmax(reinterpret_cast<const float*>(P), 1, kMaxVocab + 1, I, P, size_t(1) << 40, &ap, &err) == ORTHRUS_ERR_UNSUPPORTED_SHAPE);
+  EXPECT(check_argmax(reinterpret_cast<const float*>(P), 1, kMaxVocab, I, P, size_t(1) << 40, &ap, &err) == ORTHRUS_OK);
+  EXPECT(int64_t(ap.chunk) * (ap.nchunks - 1) + ap.chunk < (int64_t(1) << 31));
+  EXPECT(!plan_lmhead(1, 4096, kMaxVocab + 1, &lp0, nullptr));
   EXPECT(check_accept(reinterpret_cast<const float*>(P), I, 1, 32, 1024, const_cast<int32_t*>(I), const_cast<int32_t*>(I), const_cast<int32_t*>(I), nullptr, P, 1 << 20, &ap, &err) == ORTHRUS_ERR_INVALID_ARG);
   EXPECT(check_accept(reinterpret_cast<const float*>(P), I, 1, 65, 1024, const_cast<int32_t*>(I), const_cast<int32_t*>(I), const_cast<int32_t*>(I), const_cast<int32_t*>(I), P, 1 << 20, &ap, &err) == ORTHRUS_ERR_UNSUPPORTED_SHAPE);
 
@@ -85,6 +91,8 @@ int main() {
   EXPECT(plan_sample(32, 0, 151936, &sp) && sp.chunk == 4096 && sp.nchunks == 38);
   EXPECT(plan_sample(1, 0, 4200000, &sp) && sp.chunk == 4096 && sp.nchunks == 1026);
   EXPECT(plan_sample(2, 0, 4200000, &sp) && sp.chunk <= kSampleMaxChunk && sp.nchunks <= 1024);
+  EXPECT(check_sample(reinterpret_cast<const float*>(P), 1, kMaxVocab + 1, 1.0f, reinterpret_cast<const float*>(P), I, P, size_t(1) << 40, &sp, &err) == ORTHRUS_ERR_UNSUPPORTED_SHAPE);
+  EXPECT(check_accept_sampled(reinterpret_cast<const float*>(P), reinterpret_cast<const float*>(P), I, 1, 32, kMaxVocab + 1, 1.0f, reinterpret_cast<const float*>(P), reinterpret_cast<const float*>(P), I, I, I, I, P, size_t(1) << 40, &sp, &err) == ORTHRUS_ERR_UNSUPPORTED_SHAPE);
 
   int32_t* O = reinterpret_cast<int32_t*>(uintptr_t(0x30000));
   const int64_t pool = int64_t(4096) * 8 * 16 * 128;

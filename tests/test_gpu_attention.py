@@ -74,20 +74,14 @@ def test_qwen3_8b_40k_sharp(lib, mode):
     compare(run(lib, c, mode), oracle(c, mode), f"40k {mode}")
 
 
-def test_ragged16_sampled_sequences(lib):
-    # batch 16, L_b ~ U[1024, 32768], K 32; the oracle checks 4 of the 16 sequences
+def test_ragged16_all_sequences(lib):
+    # batch 16, L_b ~ U[1024, 32768], K 32: every sequence, every row against the oracle
     from synth import ragged_lengths
-    from oracle import block_attention
     lens = ragged_lengths(4, 16)
     c = case(4, 16, 32, 32, 8, 128, lens, sharp=True)
     for mode in ("draft", "verify"):
         print(f"ragged16 {mode}", flush=True)
-        out = run(lib, c, mode)
-        q, kb, vb, kp, vp, table, sl = oracle_inputs(c)
-        for b in (0, 5, 11, 15):
-            ref = block_attention(q[b:b + 1], kb[b:b + 1], vb[b:b + 1], kp, vp, table[b:b + 1],
-                                  sl[b:b + 1], mode)
-            compare(out[b:b + 1], ref, f"ragged16 {mode} seq {b}")
+        compare(run(lib, c, mode), oracle(c, mode), f"ragged16 {mode}")
 
 
 def test_k1_is_decode_and_masks_agree(lib):

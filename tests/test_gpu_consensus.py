@@ -111,10 +111,13 @@ def test_accept_golden_cases(lib):
     ([0, 15, 16, 37], 8, 3, 64),
     ([40960], 32, 2, 128),          # 40K context: two freshly allocated pages
     ([1, 1024, 30000, 77, 4095], 32, 1, 128),
+    ("ragged16", 32, 2, 128),       # batch 16, L_b ~ U[1024, 32768]
 ])
 def test_commit_matches_oracle(lib, lens, K, layers, D):
     from oracle import commit_kv
-    from synth import make_paged_case
+    from synth import make_paged_case, ragged_lengths
+    if lens == "ragged16":
+        lens = ragged_lengths(4, 16)
     B = len(lens)
     Hkv = 8 if D == 128 else 2
     c = make_paged_case(21, B, K, 4 * Hkv, Hkv, D, lens, layers=layers, fill="sentinel")

@@ -192,15 +192,13 @@ def test_k1_decode_and_last_row(lib):
     assert torch.equal(d[:, -1].view(torch.int16), v[:, -1].view(torch.int16))
 
 
-def test_ragged16_sampled_sequences(lib):
+def test_ragged16_all_sequences(lib):
     from synth import ragged_lengths
     c = case(47, 16, 32, 32, 8, ragged_lengths(47, 16), sharp=True)
     f = to_fp8(c)
     for mode in ("draft", "verify"):
         print(f"fp8 ragged16 {mode}", flush=True)
-        out = run_fp8(lib, c, f, mode)
-        for b in (0, 6, 15):
-            compare(out[b:b + 1], oracle_fp8(c, f, mode, rows=slice(b, b + 1)), f"fp8 ragged16 {mode} seq {b}")
+        compare(run_fp8(lib, c, f, mode), oracle_fp8(c, f, mode), f"fp8 ragged16 {mode}")
 
 
 def test_verify_row_is_batch_invariant(lib):

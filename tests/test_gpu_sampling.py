@@ -148,3 +148,26 @@ def test_rejects_bad_temperature_and_small_workspace(lib):
         lib.orthrus_sample(z, 0.0, u, out)
     with pytest.raises(lib.OrthrusError, match="WORKSPACE_TOO_SMALL"):
         lib.orthrus_sample(z, 1.0, u, out, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+
+
+def test_empty_residual_draws_from_the_ar_distribution(lib):
+    """Equal views (p == q) and drafted tokens whose logit sits 1000 below the
+    row maximum: p = q = 0 in fp64 for them, so the row is rejected and the
+    residual max(0, p - q) is empty.  The emitted token must be the oracle's
+    draw from p with u_res (the kernel's fallback path)."""
+    from oracle.sampling import speculative_accept
+    rng = np.random.default_rng(11)
+    B, K, V = 3, 32, 151936
+    z = llm_logits(rng, (B, K, V))
+    d = z.argmax(-1).astype(np.int32)                # accepted rows: each row's most likely token
+    for b, j in enumerate((0, 7, 31)):               # first zero-probability draft at row j
+        tok = int(rng.integers(0, V))
+        z[b, j, tok] = z[b, j].max() - np.float32(1000.0)
+        d[b, j] = tok
+    u_acc = uniforms(rng, (B, K)) * np.float32(0.5)  # rows with p = q > 0 are accepted
+    u_res = uniforms(rng, (B, K))
+    tok, n_acc, n_emit, nxt = run_accept(lib, z, z, d, 1.0, u_acc, u_res)
+    r_tok, r_acc, r_emit, r_nxt = speculative_accept(z, z, d, 1.0, u_acc, u_res)
+    assert list(r_acc) == [0, 7, 31]
+    assert np.array_equal(n_acc, r_acc) and np.array_equal(n_emit, r_emit) and np.array_equal(nxt, r_nxt)
+    assert np.array_equal(tok, r_tok)

@@ -117,3 +117,23 @@ def test_residual_excludes_the_rejected_token_when_the_draft_overweights_it():
     assert n_acc[0] == 0 and n_emit[0] == 1 and tok[0, 0] == 1 and nxt[0] == 1   # 0.7 * 0.6 > 0.4
     tok, n_acc, _, _ = speculative_accept(zd[None], za[None], d, 1.0, np.array([[0.2]]), np.array([[0.7]]))
     assert n_acc[0] == 1 and tok[0, 0] == 2                                          # 0.2 * 0.8 < 0.2
+
+
+def test_empty_residual_draws_from_the_ar_distribution():
+    """The views agree exactly (p == q) and the drafted token has probability
+    0 in both: exp underflows to 0 in fp64 for a logit 1000 below the row
+    maximum.  The acceptance test 0 * u < 0 fails, so the row is rejected,
+    and the residual max(0, p - q) is 0 everywhere.  The emitted token is
+    then drawn from p itself.  Hand-worked: p = q = [1/4, 3/4, 0]."""
+    z = np.array([[[0.0, np.log(3.0), -1000.0]]])
+    d = np.array([[2]])
+    assert softmax_t(z[0, 0], 1.0)[2] == 0.0
+    for u_res, want in ((0.0, 0), (0.2, 0), (0.2499, 0), (0.2501, 1), (0.9, 1)):
+        tok, n_acc, n_emit, nxt = speculative_accept(z, z, d, 1.0, np.array([[0.3]]), np.array([[u_res]]))
+        assert (n_acc[0], n_emit[0], tok[0, 0], nxt[0]) == (0, 1, want, want), u_res
+    # the same with two rows: row 0 is accepted (a token of positive weight,
+    # equal views), row 1 has the zero-probability draft
+    z2 = np.concatenate([z, z], axis=1)
+    tok, n_acc, n_emit, nxt = speculative_accept(z2, z2, np.array([[1, 2]]), 1.0, np.array([[0.99, 0.5]]),
+                                                 np.array([[0.0, 0.6]]))
+    assert (n_acc[0], n_emit[0], list(tok[0]), nxt[0]) == (1, 2, [1, 1], 1)
