@@ -49,6 +49,8 @@ def parse_args():
     p.add_argument("--pools", type=int, default=0, help="KV pool copies to rotate (0 = auto)")
     p.add_argument("--split", type=int, default=0, help="split_tokens override (0 = library choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra-workloads", action="store_true",
+                   help="skip the 4K and 16-sequence ragged objects of the default (40K) run")
     p.add_argument("--no-graph", dest="graph", action="store_false",
                    help="launch the timed steps eagerly instead of replaying HIP graphs")
     p.add_argument("--cpu-steps", type=int, default=3)
@@ -187,8 +189,15 @@ def main():
                               inv[table0.long()].to(torch.int32).contiguous(), seq_lens))
     q_d, kb_d, vb_d = (to_dev16(torch, np, x) for x in (case.q, case.k_blk, case.v_blk))
     q_v, kb_v, vb_v = (to_dev16(torch, np, x) for x in (qv, kbv, vbv))
-    logits_d = torch.from_numpy(cons.logits_d).to(dev)
-    logits_a = torch.from_numpy(cons.logits_a).to(dev)
+    # the consensus reads rotating logits buffers (8 per view: 156 MB per view
+    # at B = 1, more than the Infinity Cache holds next to the KV stream), as a
+    # real step reads the LM head's fresh output; the copies hold the same
+    # planted values, so every step has the drawn accepted lengths
+    n_logits = 8
+    logits_d0 = torch.from_numpy(cons.logits_d).to(dev)
+    logits_a0 = torch.from_numpy(cons.logits_a).to(dev)
+    logits_ds = [logits_d0] + [logits_d0.clone() for _ in range(n_logits - 1)]
+    logits_as = [logits_a0] + [logits_a0.clone() for _ in range(n_logits - 1)]
     out_d = torch.empty_like(q_d)
     out_v = torch.empty_like(q_v)
     d_tok = torch.empty((B, K), dtype=torch.int32, device=dev)
@@ -205,10 +214,11 @@ def main():
         s_ = torch.cuda.current_stream()      # the capture stream while a graph is recorded
         dv.orthrus_attn_draft(kv, q_d, kb_d, vb_d, out_d, max_ctx=max_ctx, split_tokens=args.split,
                               workspace=ws_attn, stream=s_)
-        dv.orthrus_argmax(logits_d, d_tok, workspace=ws_arg, stream=s_)
+        dv.orthrus_argmax(logits_ds[i % n_logits], d_tok, workspace=ws_arg, stream=s_)
         dv.orthrus_attn_verify(kv_v, q_v, kb_v, vb_v, out_v, max_ctx=max_ctx, split_tokens=args.split,
                                workspace=ws_attn, stream=s_)
-        dv.orthrus_accept(logits_a, d_tok, a_tok, n_acc, n_emit, nxt, workspace=ws_arg, stream=s_)
+        dv.orthrus_accept(logits_as[i % n_logits], d_tok, a_tok, n_acc, n_emit, nxt, workspace=ws_arg,
+                          stream=s_)
         dv.orthrus_commit_kv(kv_v, kb_commit, vb_commit, n_emit, lens_out, stream=s_)
 
     # the first warmup steps run eagerly (they also initialise everything the
@@ -230,11 +240,26 @@ def main():
     # Each step is replayed from a HIP graph of the same five library calls, so
     # the GPU runs the kernels back to back without host gaps.  Draft and
     # verify read different pool copies; the graphs cycle through the copies.
-    n_graphs = max(1, n_pools // 2) if args.graph else 0
+    n_graphs = max(1, n_pools // 2, n_logits) if args.graph else 0
     graphs = [capture(lambda j=j: step(j)) for j in range(n_graphs)]
     torch.cuda.synchronize()
     for i in range(n_eager, args.warmup):          # the remaining warmup steps
-        graphs[i % n_graphs].replay()
+        if args.graph:
+            graphs[i % n_graphs].replay()
+        else:
+            step(i)
+    # settle the clocks whatever --warmup says: at least 40 ms of untimed steps
+    # (a few steps leave the shader clock ramping and read ~10 % slow)
+    torch.cuda.synchronize()
+    t_settle, n_settle = time.perf_counter(), 0
+    while time.perf_counter() - t_settle < 0.04 or n_settle < 8:
+        if args.graph:
+            graphs[n_settle % n_graphs].replay()
+        else:
+            step(n_settle)
+        n_settle += 1
+        if n_settle % 8 == 0:
+            torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
@@ -253,11 +278,12 @@ def main():
         "draft_attn": lambda i: dv.orthrus_attn_draft(kvs[(2 * i) % n_pools], q_d, kb_d, vb_d, out_d,
                                                       max_ctx=max_ctx, split_tokens=args.split,
                                                       workspace=ws_attn, stream=None),
-        "draft_argmax": lambda i: dv.orthrus_argmax(logits_d, d_tok, workspace=ws_arg, stream=None),
+        "draft_argmax": lambda i: dv.orthrus_argmax(logits_ds[i % n_logits], d_tok, workspace=ws_arg,
+                                                    stream=None),
         "verify_attn": lambda i: dv.orthrus_attn_verify(kvs[(2 * i + 1) % n_pools], q_v, kb_v, vb_v, out_v,
                                                         max_ctx=max_ctx, split_tokens=args.split,
                                                         workspace=ws_attn, stream=None),
-        "accept": lambda i: dv.orthrus_accept(logits_a, d_tok, a_tok, n_acc, n_emit, nxt,
+        "accept": lambda i: dv.orthrus_accept(logits_as[i % n_logits], d_tok, a_tok, n_acc, n_emit, nxt,
                                               workspace=ws_arg, stream=None),
         "commit": lambda i: dv.orthrus_commit_kv(kvs[(2 * i + 1) % n_pools], kb_commit, vb_commit, n_emit,
                                                  lens_out, stream=None),
@@ -310,10 +336,12 @@ def main():
         tok_s = torch.empty((B, K), dtype=torch.int32, device=dev)
         ws_samp = torch.empty(dv.orthrus_sample_workspace_bytes(B * K, V), dtype=torch.uint8, device=dev)
         ws_accs = torch.empty(dv.orthrus_accept_sampled_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
-        op_calls["draft_sample_t1"] = lambda i: dv.orthrus_sample(logits_d, 1.0, u_draft, d_tok, workspace=ws_samp,
+        op_calls["draft_sample_t1"] = lambda i: dv.orthrus_sample(logits_ds[i % n_logits], 1.0, u_draft, d_tok,
+                                                                  workspace=ws_samp,
                                                                   stream=None)
         op_calls["accept_sampled_t1"] = lambda i: dv.orthrus_accept_sampled(
-            logits_d, logits_a, d_tok, 1.0, u_acc, u_res, tok_s, n_acc, n_emit, nxt, workspace=ws_accs,
+            logits_ds[i % n_logits], logits_as[i % n_logits], d_tok, 1.0, u_acc, u_res, tok_s, n_acc, n_emit, nxt,
+            workspace=ws_accs,
             stream=None)
         op_calls["quantize_block_kv"] = lambda i: dv.orthrus_quantize_kv(kb_v, vb_v, scale, scale, kb8_v, vb8_v,
                                                                          stream=None)
@@ -373,7 +401,14 @@ def main():
                    if args.split == 0 else args.split, "kv_pool_copies": n_pools},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "steps_per_s": round(1e3 / ms_per_step, 1),
-        "tokens_per_step_expected": round(float(sum(min(int(a) + 1, K) for a in cons.n_acc)), 2),
+        # emitted tokens per step: the timed step's own drawn accepted lengths,
+        # and the expectation under geometric(0.15) acceptance (per sequence
+        # sum_{k<K} 0.85^k = 6.63 at K = 32)
+        "tokens_per_step": {
+            "realised": int(sum(min(int(a) + 1, K) for a in cons.n_acc)),
+            "expected": round(B * sum(0.85 ** k for k in range(K)), 2),
+        },
+        "settle": {"warmup_steps": args.warmup, "settle_steps": n_settle, "settle_min_ms": 40},
         "op_ms": {k: round(v, 4) for k, v in op_ms.items()},
         "timing": "HIP graph replay" if args.graph else "eager launches",
         "attn_kv_gbps": {o: round(kv_bytes / (op_ms[o] * 1e-3) / 1e9, 1)
@@ -433,9 +468,151 @@ def main():
                         "accept_sampled_t1": round(2 * logit_bytes / (op_ms["accept_sampled_t1"] * 1e-3) / 1e9, 1)},
         "note": "fp32 logits read once per statistics pass; fp64 exponentials",
     }
+    if args.workload == "qwen3_8b_40k" and not args.no_extra_workloads:
+        res["qwen3_8b_4k"] = workload_object(args, torch, dv, synth, "qwen3_8b_4k")
+        res["qwen3_8b_ragged16"] = workload_object(args, torch, dv, synth, "qwen3_8b_ragged16")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, case, (qv, kbv, vbv), cons, kv_bytes)
     print(json.dumps(res), flush=True)
+
+
+def time_graph(torch, graph, reps):
+    """Replay a captured graph for at least 40 ms (settled clocks), then
+    return the median of 9 timed replays, in ms per call (reps calls each)."""
+    torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < 0.04:
+        graph.replay()
+        torch.cuda.synchronize()
+    samples = []
+    stream = torch.cuda.current_stream()
+    for _ in range(9):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        samples.append(e0.elapsed_time(e1) / reps)
+    return statistics.median(samples)
+
+
+def workload_object(args, torch, dv, synth, name):
+    """Draft and verify attention, the consensus and the commit of another
+    workload (the 4K single sequence or the 16-sequence ragged batch), with
+    inputs drawn on the device from a seeded generator: K/V N(0, 1/sqrt(D))
+    in independently permuted pool copies (at least 1.3 GB in all), planted
+    argmax logits with geometric(0.15) accepted lengths in 8 rotating buffers
+    per view.  Per-op times are graph replays of 16 calls; the step time is
+    graph replays of whole steps."""
+    import numpy as np
+    w = synth.WORKLOADS[name]
+    B, K, Hq, Hkv, D, V = w["B"], w["K"], w["Hq"], w["Hkv"], w["D"], w["V"]
+    lens = np.asarray(w["seq_lens"] if w["seq_lens"] is not None else synth.ragged_lengths(w["seed"], B),
+                      dtype=np.int64)
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(w["seed"] + 31)
+    per_seq = [-(-(int(l) + K) // 16) for l in lens]
+    maxp = max(per_seq) + 1
+    npages = sum(per_seq) + 8
+    sd = 1.0 / math.sqrt(D)
+    kp = (torch.randn((npages, Hkv, 16, D), generator=g, device=dev) * sd).to(torch.bfloat16)
+    vp = (torch.randn((npages, Hkv, 16, D), generator=g, device=dev) * sd).to(torch.bfloat16)
+    n_pools = max(2, min(128, math.ceil(1.3e9 / (2 * kp.numel() * 2))))
+    seq = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    kvs = []
+    for c in range(n_pools):
+        perm = torch.randperm(npages, generator=g, device=dev).to(torch.int32)
+        table = torch.full((B, maxp), int(perm[-1]), dtype=torch.int32, device=dev)
+        o = 0
+        for b, n in enumerate(per_seq):
+            table[b, :n] = perm[o:o + n]
+            o += n
+        kvs.append(dv.PagedKV(kp if c == 0 else kp.clone(), vp if c == 0 else vp.clone(), table, seq))
+    q = [(torch.randn((B, K, Hq, D), generator=g, device=dev) * sd).to(torch.bfloat16) for _ in range(2)]
+    kb = [(torch.randn((B, K, Hkv, D), generator=g, device=dev) * sd).to(torch.bfloat16) for _ in range(2)]
+    vb = [(torch.randn((B, K, Hkv, D), generator=g, device=dev) * sd).to(torch.bfloat16) for _ in range(2)]
+    out = [torch.empty_like(q[0]) for _ in range(2)]
+    # planted consensus: the draft agrees with the AR view on the drawn n_acc
+    # positions of every sequence, the next position differs
+    rng = np.random.default_rng(w["seed"] + 32)
+    n_acc_drawn = synth.draw_accept_lengths(rng, B, K, "geometric", 0.15)
+    a_idx = rng.integers(0, V, size=(B, K))
+    d_idx = rng.integers(0, V, size=(B, K))
+    for b in range(B):
+        j = int(n_acc_drawn[b])
+        d_idx[b, :j] = a_idx[b, :j]
+        if j < K:
+            d_idx[b, j] = (a_idx[b, j] + 1 + rng.integers(0, V - 1)) % V
+    bi = torch.arange(B, device=dev)[:, None].expand(B, K)
+    ki = torch.arange(K, device=dev)[None, :].expand(B, K)
+
+    def planted(idx):
+        x = torch.randn((B, K, V), generator=g, device=dev).clamp_(-8.0, 8.0)
+        x[bi, ki, torch.from_numpy(idx).to(dev)] = 9.0 + torch.rand((B, K), generator=g, device=dev)
+        return x
+    n_logits = 8
+    lds = [planted(d_idx) for _ in range(n_logits)]
+    las = [planted(a_idx) for _ in range(n_logits)]
+    max_ctx = int(lens.max())
+    ws_attn = dv.attn_workspace(kvs[0], q[0], max_ctx, 0)
+    ws_arg = dv.argmax_workspace(B * K, V, dev)
+    d_tok, a_tok = (torch.empty((B, K), dtype=torch.int32, device=dev) for _ in range(2))
+    n_acc, n_emit, nxt, lens_out = (torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4))
+    ops = {
+        "draft_attn": lambda i: dv.orthrus_attn_draft(kvs[(2 * i) % n_pools], q[0], kb[0], vb[0], out[0],
+                                                      max_ctx=max_ctx, workspace=ws_attn, stream=None),
+        "draft_argmax": lambda i: dv.orthrus_argmax(lds[i % n_logits], d_tok, workspace=ws_arg, stream=None),
+        "verify_attn": lambda i: dv.orthrus_attn_verify(kvs[(2 * i + 1) % n_pools], q[1], kb[1], vb[1], out[1],
+                                                        max_ctx=max_ctx, workspace=ws_attn, stream=None),
+        "accept": lambda i: dv.orthrus_accept(las[i % n_logits], d_tok, a_tok, n_acc, n_emit, nxt,
+                                              workspace=ws_arg, stream=None),
+        "commit": lambda i: dv.orthrus_commit_kv(kvs[(2 * i + 1) % n_pools], kb[1][None], vb[1][None], n_emit,
+                                                 lens_out, stream=None),
+    }
+    for i in range(2):                      # eager: initialises everything the graphs capture
+        for op in ops.values():
+            op(i)
+    torch.cuda.synchronize()
+    assert torch.equal(n_acc.cpu(), torch.from_numpy(np.asarray(n_acc_drawn, dtype=np.int32))), "accept mismatch"
+
+    def capture(fn):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        return graph
+    REPS = 16
+    op_ms = {op: time_graph(torch, capture(lambda call=call: [call(i) for i in range(REPS)]), REPS)
+             for op, call in ops.items()}
+    n_steps = 8                              # one graph of 8 whole steps (rotating copies)
+    ms_per_step = time_graph(torch, capture(lambda: [ops[o](j) for j in range(n_steps) for o in ops]), n_steps)
+    kv_bytes = 4 * Hkv * D * int(lens.sum())
+    pages_read = int(sum(-(-int(l) // 16) for l in lens))
+    attn_bytes = kv_bytes + 2 * B * K * Hq * D * 2 + 2 * 2 * B * K * Hkv * D * 2 + 4 * pages_read + 4 * B
+    attn_flops = 4.0 * Hq * K * D * float(sum(int(l) + K for l in lens))
+    dom = max(("draft_attn", "verify_attn"), key=lambda o: op_ms[o])
+    dom_s = op_ms[dom] * 1e-3
+    res = {
+        "config": {"workload": name, "batch": B, "context": [int(x) for x in lens] if B > 1 else int(lens[0]),
+                   "block_k": K, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "vocab": V,
+                   "split_tokens": dv.orthrus_attn_split_tokens(B, Hkv, max_ctx), "kv_pool_copies": n_pools},
+        "data": "synthetic, drawn on the device (seeded): K/V N(0,1/sqrt(D)), planted-argmax logits with "
+                "geometric(0.15) accepted lengths",
+        "op_ms": {k: round(v, 4) for k, v in op_ms.items()},
+        "ms_per_step": round(ms_per_step, 4),
+        "steps_per_s": round(1e3 / ms_per_step, 1),
+        "kv_gbps_per_step": round(2 * kv_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "tokens_per_step": {"realised": int(sum(min(int(a) + 1, K) for a in n_acc_drawn)),
+                            "expected": round(B * sum(0.85 ** k for k in range(K)), 2)},
+        "attn_kv_gbps": {o: round(kv_bytes / (op_ms[o] * 1e-3) / 1e9, 1) for o in ("draft_attn", "verify_attn")},
+        "roofline": {"kernel": f"{dom}: attn_split_kernel + attn_combine_kernel (one ABI call)", "bound": "hbm",
+                     "achieved": round(attn_bytes / dom_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(attn_bytes / dom_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": attn_bytes,
+                     "mfma_tflops": round(attn_flops / dom_s / 1e12, 1)},
+    }
+    del kvs, kp, vp, lds, las
+    torch.cuda.empty_cache()
+    return res
 
 
 def e2e(args, torch, dv, synth):
@@ -503,10 +680,22 @@ def e2e(args, torch, dv, synth):
     return res
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(args, case, vqkv, cons, kv_bytes):
     """The CPU oracle (fp64 numpy) timed on this host over the same workload:
     a bounded sample of whole steps (draft + verify attention over every head,
-    both argmaxes, acceptance, commit)."""
+    both argmaxes, acceptance, commit), with every BLAS thread the process may
+    use, then one step on a single thread."""
     import numpy as np
     import threadpoolctl
 
@@ -514,8 +703,8 @@ def cpu_baseline(args, case, vqkv, cons, kv_bytes):
     qv, kbv, vbv = vqkv
     f = oracle.from_bf16
     kp, vp = f(case.k_pages[0]), f(case.v_pages[0])
-    times = []
-    for _ in range(max(1, args.cpu_steps)):
+
+    def one_step():
         t = time.perf_counter()
         oracle.block_attention(f(case.q), f(case.k_blk), f(case.v_blk), kp, vp, case.block_table,
                                case.seq_lens, "draft")
@@ -525,14 +714,27 @@ def cpu_baseline(args, case, vqkv, cons, kv_bytes):
         _, n_emit, _ = oracle.accept(d, a)
         oracle.commit_kv(case.k_pages[:1], case.v_pages[:1], case.block_table, case.seq_lens,
                          kbv[None], vbv[None], n_emit)
-        times.append(time.perf_counter() - t)
+        return time.perf_counter() - t
+
+    times = [one_step() for _ in range(max(1, args.cpu_steps))]
     sec = statistics.median(times)
     threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    with threadpoolctl.threadpool_limits(limits=1):
+        sec1 = one_step()
+    try:
+        affinity = sorted(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = list(range(os.cpu_count() or 1))
     return {"value": round(2 * kv_bytes / sec / 1e9, 3), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle", "seconds_per_step": round(sec, 3),
             "steps_per_s": round(1.0 / sec, 4),
-            "sample": f"{len(times)} whole steps of the {args.workload} workload (median), "
-                      f"numpy fp64, {threads} BLAS threads on {os.cpu_count()} visible CPUs"}
+            "single_thread": {"seconds_per_step": round(sec1, 3), "value": round(2 * kv_bytes / sec1 / 1e9, 3),
+                              "unit": "GB/s"},
+            "cpu_model": cpu_model(), "affinity": f"{len(affinity)} CPUs: {affinity[0]}-{affinity[-1]}"
+            if affinity and affinity[-1] - affinity[0] + 1 == len(affinity) else str(affinity),
+            "sample": f"{len(times)} whole steps of the {args.workload} workload (median) with {threads} "
+                      f"BLAS threads on {len(affinity)} CPUs the process may use, then 1 step on 1 thread; "
+                      f"numpy fp64"}
 
 
 if __name__ == "__main__":

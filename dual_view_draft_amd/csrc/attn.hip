@@ -9,7 +9,8 @@
 // compile-time mask.
 //
 // Work decomposition (flash-decoding style split context):
-//   grid = (context split s, KV head g x row chunk, sequence b), one
+//   one workgroup per (context split s, sequence b, KV head g, row chunk),
+//   (b, g, chunk) fastest so that all splits of a head share an XCD; one
 //   8-wavefront workgroup per CU.  A workgroup owns the G*K query rows of KV
 //   head g (up to 128 rows per chunk) and streams the keys/values at absolute
 //   positions [s*split, (s+1)*split) in 64-token tiles (4 pages), so every K/V
@@ -184,10 +185,18 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char ring[NS * STAGE_BYTES];
   auto stage = [&](int k) { return ring + k * STAGE_BYTES; };
 
-  const int s = blockIdx.x;
-  const int g = blockIdx.y / a.nchunks;
-  const int chunk = blockIdx.y - g * a.nchunks;
-  const int b = blockIdx.z;
+  // Linear workgroup id -> (split s, sequence b, KV head g, row chunk).  The
+  // (b, g, chunk) index runs fastest, so with the 8 KV heads of the 8B shape
+  // every split of head g gets an id = g (mod 8): the dispatcher deals ids to
+  // the eight XCDs in turn, so one XCD streams one head and the Q rows and
+  // page ids that all splits of the head read come from that XCD's L2.
+  const int ny = a.Hkv * a.nchunks * a.B;
+  const int s = blockIdx.x / ny;
+  const int yz = blockIdx.x - s * ny;
+  const int b = yz / (a.Hkv * a.nchunks);
+  const int yy = yz - b * (a.Hkv * a.nchunks);
+  const int g = yy / a.nchunks;
+  const int chunk = yy - g * a.nchunks;
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, col = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
@@ -615,8 +624,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
   constexpr int U = 8;            // splits per lane group per batch
   constexpr int BATCH = U * SG;   // splits per batch
   const int lane = threadIdx.x & 63;
-  const int orow = blockIdx.x * 4 + (threadIdx.x >> 6);   // (b, i, h) flattened
-  if (orow >= a.B * a.K * a.Hq) return;                    // uniform per wavefront
+  // Workgroup -> (sequence b, KV head g) = id mod (B * Hkv), and 4 of that
+  // head's G*K rows: the merge of head g runs on the XCD whose L2 took the
+  // head's partial results (as in the split kernel's mapping).
+  const int Hkv = a.Hq / a.G;
+  const int nbg = a.B * Hkv;
+  const int bg = blockIdx.x % nbg;
+  const int rr = (blockIdx.x / nbg) * 4 + (threadIdx.x >> 6);   // row of head (b, g): i * G + gg
+  if (rr >= a.K * a.G) return;                                   // uniform per wavefront
+  const int orow = ((bg / Hkv) * a.K + rr / a.G) * a.Hq + (bg % Hkv) * a.G + rr % a.G;   // (b, i, h) flattened
   const int sg = lane / TPR;
   const int d0 = (lane % TPR) * 8;
   const int h = orow % a.Hq;
@@ -627,7 +643,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
   const int r = i * a.G + (h - g * a.G);
   const int chunk = r / kMaxRowsPerCta;
   const int rl = r - chunk * kMaxRowsPerCta;
-  const int Hkv = a.Hq / a.G;
   const size_t prow0 = ((size_t(b) * Hkv + g) * a.nchunks + chunk) * a.nsplit * a.rpc + rl;
   const float* ml = a.part_ml + prow0 * 2;
   const uint16_t* po = a.part_o + prow0 * D + d0;
@@ -706,7 +721,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
 
 template <int D, bool VERIFY, bool FP8>
 hipError_t launch_split(const AttnArgs& a, hipStream_t stream) {
-  dim3 grid(a.nsplit, a.Hkv * a.nchunks, a.B);
+  dim3 grid(unsigned(int64_t(a.nsplit) * a.Hkv * a.nchunks * a.B));
   return launch_kernel(&attn_split_kernel<D, VERIFY, FP8>, grid, dim3(512), stream, a);
 }
 
@@ -747,8 +762,7 @@ hipError_t launch_attention(const AttnPlan& p, const orthrus_kv& kv, const void*
   c.out = static_cast<uint16_t*>(out);
   c.B = p.B; c.K = p.K; c.Hq = p.Hq; c.G = p.G; c.max_ctx = p.max_ctx;
   c.split = p.split; c.nsplit = p.nsplit; c.nchunks = p.nchunks; c.rpc = p.rows_per_chunk;
-  const int64_t rows = int64_t(p.B) * p.K * p.Hq;
-  dim3 grid(unsigned((rows + 3) / 4));
+  dim3 grid(unsigned((int64_t(p.K) * p.G + 3) / 4 * p.B * p.Hkv));
   return p.D == 128 ? launch_kernel(&attn_combine_kernel<128>, grid, dim3(256), stream, c)
                     : launch_kernel(&attn_combine_kernel<64>, grid, dim3(256), stream, c);
 }

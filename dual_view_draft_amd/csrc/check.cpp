@@ -1,6 +1,7 @@
 // Host-side argument checking and launch planning (see check.h).
 #include "check.h"
 
+#include <climits>
 #include <cmath>
 #include <cstdio>
 
@@ -57,15 +58,34 @@ const char* status_string(int status) {
 
 int attn_split_tokens(int B, int Hkv, int max_ctx) {
   if (B < 1 || Hkv < 1 || max_ctx < 0) return kTile * 4;
-  // One 8-wavefront workgroup fills a CU (256 CUs).  A single sequence is cut
-  // into about one split per CU; a batch (whose lengths the host does not
-  // know) into about four per CU, so that short and long sequences balance.
-  const int64_t work = int64_t(B) * Hkv * (int64_t(max_ctx) + kTile);
-  const int64_t target = B == 1 ? 256 : 1024;
-  int64_t s = round_up(ceil_div(work, target), kTile);
-  if (s < 2 * kTile) s = 2 * kTile;
-  if (s > kMaxSplitTiles * kTile) s = kMaxSplitTiles * kTile;
-  return int(s);
+  constexpr int64_t kCUs = 256;   // one 8-wavefront workgroup fills a CU of an MI355X
+  if (B == 1) {
+    // A single sequence is cut into about one split per CU.
+    int64_t s = round_up(ceil_div(int64_t(Hkv) * (int64_t(max_ctx) + kTile), kCUs), kTile);
+    if (s < 2 * kTile) s = 2 * kTile;
+    if (s > kMaxSplitTiles * kTile) s = kMaxSplitTiles * kTile;
+    return int(s);
+  }
+  // A batch: the host knows only the longest length.  Taking the lengths as
+  // uniform on [0, max_ctx], a split of s tokens gives about
+  //   W(s) = B * Hkv * ((max_ctx / 2 + kTile / 2) / s + 1 / 2)
+  // active workgroups, which run in ceil(W / 256) rounds of one workgroup per
+  // CU, each round as long as one split.  The split with the fewest
+  // round-tokens ceil(W / 256) * s wins (the longer split on ties: fewer
+  // partial results to merge), searched over 1024 .. 4096 tokens.
+  int64_t best_s = 0, best_cost = 0;
+  for (int64_t sp = 16 * kTile; sp <= kMaxSplitTiles * kTile; sp += kTile) {
+    const double w = double(B) * Hkv * ((0.5 * max_ctx + 0.5 * kTile) / double(sp) + 0.5);
+    const int64_t cost = int64_t(std::ceil(w / double(kCUs))) * sp;
+    if (best_s == 0 || cost <= best_cost) {
+      best_s = sp;
+      best_cost = cost;
+    }
+  }
+  // a short context needs no more than one split per sequence
+  const int64_t whole = round_up(int64_t(max_ctx) + kTile, kTile);
+  if (whole < best_s) best_s = whole < 2 * kTile ? 2 * kTile : whole;
+  return int(best_s);
 }
 
 bool plan_attention_shape(int B, int K, int Hq, int Hkv, int D, int max_ctx, int split_tokens,
@@ -86,6 +106,9 @@ bool plan_attention_shape(int B, int K, int Hq, int Hkv, int D, int max_ctx, int
   p->rows = p->G * K;
   p->nchunks = int(ceil_div(p->rows, kMaxRowsPerCta));
   p->rows_per_chunk = p->rows > kMaxRowsPerCta ? kMaxRowsPerCta : int(round_up(p->rows, kRowsPerWave));
+  // one workgroup per (split, sequence, KV head, row chunk) in a 1-D grid
+  if (int64_t(B) * Hkv * p->nchunks * p->nsplit > int64_t(INT32_MAX))
+    return no("batch * num_kv_heads * context splits too large for one launch");
   const int64_t parts = int64_t(B) * Hkv * p->nchunks * p->nsplit * p->rows_per_chunk;
   p->part_o_bytes = size_t(round_up(parts * D * 2, 256));   // bf16 O / l per split row
   p->part_ml_bytes = size_t(round_up(parts * 2 * 4, 256));

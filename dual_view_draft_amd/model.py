@@ -244,7 +244,12 @@ class DualViewModel:
 
     def greedy(self, prompt: torch.Tensor, n: int, seed: int = 0, kv_scales=None):
         cache = self.new_cache(prompt.shape[0], n, seed, kv_scales)
-        toks = [self.prefill(prompt, cache)]
+        return self.decode_greedy(cache, self.prefill(prompt, cache), n)
+
+    def decode_greedy(self, cache: ModelCache, first: int, n: int):
+        """Plain greedy decoding from the cache's current state: `first` is the
+        last emitted token (not cached yet); returns n tokens starting with it."""
+        toks = [int(first)]
         out = torch.empty(1, dtype=torch.int32, device=self.device)
         t0 = time.perf_counter()
         while len(toks) < n:
@@ -257,7 +262,12 @@ class DualViewModel:
         view's draft (the draft pass still runs).  kv_scales (k, v fp32
         [layers, Hkv]) selects an e4m3 cache."""
         cache = self.new_cache(prompt.shape[0], n, seed, kv_scales)
-        toks = [self.prefill(prompt, cache)]
+        return self.decode_orthrus(cache, self.prefill(prompt, cache), n, K, drafter)
+
+    def decode_orthrus(self, cache: ModelCache, first: int, n: int, K: int = 32, drafter=None):
+        """The Orthrus loop from the cache's current state (as decode_greedy);
+        returns (n tokens, emitted tokens per step, seconds)."""
+        toks = [int(first)]
         anchor = torch.tensor([toks[0]], device=self.device)
         d, a = (torch.empty((1, K), dtype=torch.int32, device=self.device) for _ in range(2))
         n_acc, n_emit, nxt = (torch.empty(1, dtype=torch.int32, device=self.device) for _ in range(3))
@@ -273,3 +283,17 @@ class DualViewModel:
             anchor = nxt.to(torch.int64)
             emits.append(e)
         return toks[:n], emits, time.perf_counter() - t0
+
+    def block_logits(self, tokens: torch.Tensor, cache: ModelCache, view: str, mode: str,
+                     commit: bool = False) -> torch.Tensor:
+        """fp32 logits [n, V] of one block (the fused LM head's own logits, the
+        values its argmax reduces); with commit, the block's K/V (AR view)
+        are appended to the cache afterwards."""
+        hidden, k, v = self.forward(tokens, cache, view, mode)
+        n = tokens.shape[0]
+        logits = torch.empty((n, self.cfg.vocab), dtype=torch.float32, device=self.device)
+        out = torch.empty(n, dtype=torch.int32, device=self.device)
+        ob.orthrus_lmhead_argmax(hidden, self.w["lm_head"], out, logits=logits, workspace=self.ws_lm)
+        if commit:
+            cache.commit(k, v, torch.full((1,), n, dtype=torch.int32, device=self.device))
+        return logits

@@ -27,7 +27,7 @@ __all__ = [
     "PagedCase", "make_paged_case", "make_block_qkv", "ConsensusCase", "make_consensus_case",
     "draw_accept_lengths", "make_tie_logits", "ToyConfig", "TOY_CFG5", "QWEN3_8B",
     "make_model_weights_device",
-    "TOY_TINY", "make_toy_weights", "make_prompt", "WORKLOADS",
+    "TOY_TINY", "TOY_CHECK", "make_toy_weights", "make_prompt", "WORKLOADS",
 ]
 
 BF16_NAN = 0x7FC0        # quiet NaN: poison for slots no kernel may read
@@ -283,6 +283,11 @@ QWEN3_8B = ToyConfig(layers=36, hidden=4096, Hq=32, Hkv=8, D=128, ffn=12288,
                      vocab=151936, rope_base=1e6)
 TOY_TINY = ToyConfig(layers=2, hidden=64, Hq=4, Hkv=2, D=16, ffn=96,
                      vocab=97, rope_base=1e4, weight_std=0.3)
+# a small config that both the GPU models and the fp64 oracle decoder run:
+# the attention and LM-head kernels' shape limits (head_dim 64, hidden a
+# multiple of 64), Qwen3's RoPE base, several 64-row prefill blocks
+TOY_CHECK = ToyConfig(layers=2, hidden=256, Hq=8, Hkv=2, D=64, ffn=512,
+                      vocab=2048, rope_base=1e6, weight_std=0.05)
 
 
 def make_toy_weights(seed: int, cfg: ToyConfig) -> dict:

@@ -105,3 +105,50 @@ def test_fp8_cache_own_drafter_matches_greedy(setup, fp8_ref):
     scales, ref = fp8_ref
     toks, emits, _ = model.orthrus(prompt, 12, K, kv_scales=scales)
     assert toks == ref[:12]
+
+
+# ---- long context: the pages' 4K-40K regime, many splits and the merge ----
+LONG_L, LONG_N = 40960, 48
+
+
+def _teacher(ref, V, seed):
+    rng = np.random.default_rng(seed)
+
+    def teacher(out, k):
+        e = len(out)
+        d = np.array(ref[e:e + k], dtype=np.int32)
+        m = min(int(rng.geometric(0.15)) - 1, k)
+        if m < k:
+            d[m] = (d[m] + 1) % V
+        return d
+    return teacher
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_orthrus_matches_greedy_at_40k_context(setup, kv):
+    """Both loops start from the same 40960-token cache state (every layer's
+    cache filled with the same seeded values) and the same anchor: the
+    attention calls take 31 context splits and the combine, and the Orthrus
+    loop must still emit greedy decoding's tokens, with the teacher drafter
+    (every accepted length) and with the model's own drafter."""
+    from dual_view_draft_amd.model import ModelCache
+    model = setup[0]
+    cfg = model.cfg
+    scales = None
+    if kv == "e4m3":
+        s = torch.full((cfg.layers, cfg.Hkv), 1.0 / 32, dtype=torch.float32, device="cuda")
+        scales = (s, s)
+    cache = ModelCache(cfg, LONG_L + LONG_N + 3 * K + 128, "cuda", seed=4, kv_scales=scales)
+    first = 1234
+    cache.fill_random(LONG_L, seed=9)
+    ref, secs = model.decode_greedy(cache, first, LONG_N + K)
+    print(f"{kv} 40K greedy: {len(ref)} tokens in {secs:.2f} s", flush=True)
+    assert len(set(ref[:LONG_N])) > 10
+    cache.fill_random(LONG_L, seed=9)
+    toks, emits, _ = model.decode_orthrus(cache, first, LONG_N, K, drafter=_teacher(ref, cfg.vocab, 11))
+    print(f"{kv} 40K teacher drafter: {len(emits)} steps, mean emitted {np.mean(emits):.2f}", flush=True)
+    assert toks == ref[:LONG_N]
+    assert len(emits) < LONG_N // 2
+    cache.fill_random(LONG_L, seed=9)
+    toks, emits, _ = model.decode_orthrus(cache, first, 12, K)
+    assert toks == ref[:12]

@@ -79,3 +79,35 @@ def test_sensitivity_wrong_commit_breaks_losslessness(model, prompt, greedy_ref)
     bad = Bad(TOY_TINY, make_toy_weights(21, TOY_TINY), page_size=4)
     toks, _ = orthrus_generate(bad, prompt, N, K, TeacherDrafter(greedy_ref, 0.15, 5, TOY_TINY.vocab))
     assert toks != greedy_ref[:N]
+
+
+def test_planted_model_mistakes_exceed_the_gpu_bounds():
+    """The GPU models are compared with this oracle on TOY_CHECK at
+    |gpu - oracle| <= 2^-4 rms(row) (tests/test_gpu_model_oracle.py).  A
+    mistake the Orthrus == greedy checks cannot see, because both loops
+    would share it, must move the logits far past that bound: a RoPE base of
+    1e4 instead of 1e6, a doubled QK-norm gain, the wrong <mask> row."""
+    import dataclasses
+    from oracle.toy import ToyModel
+    from synth import TOY_CHECK, f32_to_bf16_bits, make_prompt, make_toy_weights
+    cfg = TOY_CHECK
+    bits = make_toy_weights(21, cfg)
+    prompt = make_prompt(21, 200, cfg.vocab)
+
+    def logits(c, b, mask_tok):
+        m = ToyModel(c, b)
+        cache = m.new_cache(200 + 96)
+        lz, k, v = m.forward(prompt, cache, "ar", "verify")
+        m.commit(cache, k, v, 200)
+        ld, _, _ = m.forward([int(prompt[-1])] + [mask_tok] * 31, cache, "diff", "draft")
+        return lz, ld
+
+    lz, ld = logits(cfg, bits, cfg.mask_id)
+    doubled = {f"l{i}.q_norm": f32_to_bf16_bits(np.full(cfg.D, 2.0, np.float32)) for i in range(cfg.layers)}
+    for name, c2, b2, mt in [("rope base", dataclasses.replace(cfg, rope_base=1e4), bits, cfg.mask_id),
+                             ("qk norm", cfg, {**bits, **doubled}, cfg.mask_id),
+                             ("mask row", cfg, bits, 5)]:
+        z2, d2 = logits(c2, b2, mt)
+        worst = max(float((np.abs(z2 - lz) / np.sqrt((lz * lz).mean(-1, keepdims=True))).max()),
+                    float((np.abs(d2 - ld) / np.sqrt((ld * ld).mean(-1, keepdims=True))).max()))
+        assert worst > 8 * 2.0 ** -4, (name, worst)
