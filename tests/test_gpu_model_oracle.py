@@ -6,18 +6,22 @@ loops share (a wrong RoPE base, QK-norm or <mask> embedding); this does.
 
 Checked: the logits of every prompt position (a 200-token prompt, four
 64-row prefill blocks through the paged cache) and of the diffusion view's
-draft block [anchor, <mask> x 31] after it.  Bounds:
-
-* ToyOrthrus (fp64 dense layers on the GPU; only the attention's q/k/v and
-  output are bf16): |gpu - oracle| <= 2^-6 * rms(row).
-* DualViewModel (the full-size model's code: every matrix product's inputs
-  and outputs bf16, fp32 accumulation, fp32 residual stream): about 20 bf16
-  roundings (relative error 2^-9 each) separate a logit from the exact
-  value across the two layers, at most about 2^-4.7 of the row's scale when
-  they all line up; the test allows 2^-4 * rms(row).
-* Greedy tokens: where the oracle's top-2 gap exceeds twice the bound, the
-  GPU's argmax must be the oracle's token (at least half of the positions
-  qualify at these seeds).
+draft block [anchor, <mask> x 31] after it.  Bound: |gpu - oracle| <=
+2^-4 * rms(row), from the bf16 roundings both GPU models make.
+* The attention kernel takes q, k, v in bf16 (relative error 2^-9 each).
+  After the QK RMSNorm |q| and |k| are at most sqrt(D), so a score
+  q.k / sqrt(D) has magnitude at most sqrt(D) = 8 and moves by at most
+  2 * 2^-9 * 8 = 2^-5: every softmax weight by a factor within e^(+-2^-5).
+  Over the two layers the hidden state, and with it every logit, can move
+  by about 2 * 2^-5 = 2^-4 of its scale.
+* DualViewModel (the full-size model's code) also rounds every matrix
+  product's inputs and outputs to bf16: about 20 more roundings of 2^-9
+  whose signs are independent, so together about sqrt(20) * 2^-9 = 2^-6.8
+  of the scale, inside the same bound; ToyOrthrus keeps its dense layers
+  in fp64.
+Greedy tokens: where the oracle's top-2 gap exceeds twice the bound, the
+GPU's argmax must be the oracle's token (at least half of the positions
+qualify at these seeds).
 
 Planted mistakes in the oracle (RoPE base 1e4, a doubled QK-norm gain, a
 wrong <mask> row) move the logits by 3-5 times the row's rms, far beyond
@@ -112,5 +116,5 @@ def test_toy_orthrus_matches_oracle(ref):
             c.commit(k, v, torch.full((1,), n, dtype=torch.int32, device="cuda"), n)
         return logits
     gz, gd = _prompt_and_draft_logits(model, cache, prompt, cfg, block)
-    _check("ToyOrthrus prefill", gz, lz, 2.0 ** -6)
-    _check("ToyOrthrus draft block", gd, ld, 2.0 ** -6)
+    _check("ToyOrthrus prefill", gz, lz, 2.0 ** -4)
+    _check("ToyOrthrus draft block", gd, ld, 2.0 ** -4)
