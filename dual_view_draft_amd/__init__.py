@@ -10,6 +10,7 @@ from .binding import (ORTHRUS_KV_BF16, ORTHRUS_KV_FP8_E4M3, ORTHRUS_MAX_BLOCK,  
                       library_path, lmhead_workspace, load_library, orthrus_abi_version,
                       orthrus_accept, orthrus_argmax, orthrus_argmax_workspace_bytes,
                       orthrus_attn_draft, orthrus_attn_split_tokens, orthrus_attn_verify,
+                      orthrus_attn_verify_noalloc,
                       orthrus_attn_workspace_bytes, orthrus_commit_kv, orthrus_last_error,
                       orthrus_lmhead_accept, orthrus_lmhead_argmax, orthrus_lmhead_workspace_bytes,
                       orthrus_quantize_kv, orthrus_status_string, orthrus_sample,

@@ -53,6 +53,9 @@ EXPORTS = {
                            [ctypes.c_int] * 3 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "orthrus_attn_verify": None,  # same signature as orthrus_attn_draft
+    "orthrus_attn_verify_noalloc": (ctypes.c_int, [ctypes.POINTER(orthrus_kv)] + [ctypes.c_void_p] * 4 +
+                                    [ctypes.c_int] * 3 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                                          ctypes.c_void_p]),
     "orthrus_argmax_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 2),
     "orthrus_argmax": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -225,6 +228,21 @@ def orthrus_attn_verify(kv: PagedKV, q, k_blk, v_blk, out, *, max_ctx: int, scal
     """Verify pass (AR view): block row i sees the cache and block rows 0..i."""
     return _attention("orthrus_attn_verify", kv, q, k_blk, v_blk, out, max_ctx, scale,
                       split_tokens, workspace, stream)
+
+
+def orthrus_attn_verify_noalloc(kv: PagedKV, q, k_blk, v_blk, out, *, max_ctx: int, scale=None,
+                                split_tokens: int = 0, stream=None):
+    """orthrus_attn_verify with the library's static scratch instead of a
+    workspace (no device allocation)."""
+    B, K, Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kvs = kv.c_struct()
+    rc = load_library().orthrus_attn_verify_noalloc(
+        ctypes.byref(kvs), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(out), B, K, Hq, float(scale),
+        int(max_ctx), int(split_tokens), _stream(stream))
+    _check(rc, "orthrus_attn_verify_noalloc")
+    return out
 
 
 def orthrus_argmax_workspace_bytes(rows: int, vocab: int) -> int:

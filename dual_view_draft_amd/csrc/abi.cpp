@@ -80,6 +80,29 @@ int orthrus_attn_verify(const orthrus_kv* kv, const void* q, const void* k_blk, 
                    split_tokens, workspace, workspace_bytes, stream, true);
 }
 
+int orthrus_attn_verify_noalloc(const orthrus_kv* kv, const void* q, const void* k_blk, const void* v_blk,
+                                void* out, int batch, int block_k, int num_q_heads, float scale,
+                                int max_ctx, int split_tokens, void* stream) {
+  try {
+    if (!kv) return fail(ORTHRUS_ERR_INVALID_ARG, "kv descriptor is null");
+    orthrus::AttnPlan plan;
+    std::string why;
+    if (orthrus::plan_attention_shape(batch, block_k, num_q_heads, kv->num_kv_heads, kv->head_dim, max_ctx,
+                                      split_tokens, &plan, &why) &&
+        plan.ws_bytes > orthrus::kStaticScratchBytes)
+      return fail(ORTHRUS_ERR_WORKSPACE_TOO_SMALL,
+                  "call needs " + std::to_string(plan.ws_bytes) + " bytes of scratch; the static scratch of "
+                  "orthrus_attn_verify_noalloc holds " + std::to_string(orthrus::kStaticScratchBytes));
+    void* scratch = nullptr;
+    const hipError_t e = orthrus::static_attn_scratch(&scratch);
+    if (e != hipSuccess) return hip_status(e);
+    return attention(kv, q, k_blk, v_blk, out, batch, block_k, num_q_heads, scale, max_ctx, split_tokens,
+                     scratch, orthrus::kStaticScratchBytes, stream, true);
+  } catch (...) {
+    return fail(ORTHRUS_ERR_HIP, "internal error");
+  }
+}
+
 size_t orthrus_argmax_workspace_bytes(int rows, int vocab) {
   orthrus::ArgmaxPlan plan;
   if (!orthrus::plan_argmax(rows, vocab, &plan)) return 0;

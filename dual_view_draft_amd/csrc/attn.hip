@@ -42,6 +42,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -726,6 +727,36 @@ hipError_t launch_split(const AttnArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Scratch of orthrus_attn_verify_noalloc: the split partials live in this
+// file-scope device array instead of a caller workspace.  Each GPU the
+// library runs on holds its own copy until the process ends; in host code
+// the name is only a stand-in, so host code uses the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept.
+namespace {
+__device__ __attribute__((aligned(256))) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t static_attn_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_attention(const AttnPlan& p, const orthrus_kv& kv, const void* q,
                             const void* k_blk, const void* v_blk, void* out, float scale,

@@ -20,6 +20,12 @@ constexpr int kMaxSplitTiles = 64;  // a context split covers at most 64 tiles (
 // the kernels' int32 index arithmetic.
 constexpr int kMaxVocab = 1 << 30;
 
+// Bytes of the static device scratch behind orthrus_attn_verify_noalloc
+// (one copy per GPU): the split partials of any call whose workspace query
+// is at most this size (every single-sequence call with 8 KV heads needs
+// about 8.6 MB).
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+
 // Geometry of one attention call, all derived on the host.
 struct AttnPlan {
   int B = 0, K = 0, Hq = 0, Hkv = 0, G = 0, D = 0;

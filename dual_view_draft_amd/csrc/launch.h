@@ -22,6 +22,10 @@ hipError_t launch_attention(const AttnPlan& plan, const orthrus_kv& kv, const vo
                             const void* k_blk, const void* v_blk, void* out, float scale,
                             bool verify, void* ws, hipStream_t stream);
 
+// Device address of the static attention scratch on the current device
+// (kStaticScratchBytes bytes), looked up once per device.
+hipError_t static_attn_scratch(void** ptr);
+
 hipError_t launch_argmax(const ArgmaxPlan& plan, const float* logits, int32_t* out, void* ws,
                          hipStream_t stream);
 

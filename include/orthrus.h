@@ -190,6 +190,24 @@ ORTHRUS_API int orthrus_attn_verify(const orthrus_kv* kv, const void* q, const v
                         int max_ctx, int split_tokens, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/*
+ * orthrus_attn_verify without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Arguments, results and errors are
+ * those of orthrus_attn_verify, computed by the same kernels; the split
+ * partial results go to a static scratch array that the library holds on
+ * each GPU (16 MiB per GPU, kept until the process ends; its address is
+ * looked up once per device on the first call there).  The call allocates
+ * nothing.  A call whose orthrus_attn_workspace_bytes(...) exceeds 16 MiB
+ * returns ORTHRUS_ERR_WORKSPACE_TOO_SMALL (every single-sequence call with
+ * 8 KV heads needs about 8.6 MB).  All calls on one GPU share the scratch:
+ * calls that may overlap on one GPU (other streams, other threads) race and
+ * must be ordered by the caller.
+ */
+ORTHRUS_API int orthrus_attn_verify_noalloc(const orthrus_kv* kv, const void* q, const void* k_blk,
+                                const void* v_blk, void* out, int batch, int block_k, int num_q_heads,
+                                float scale, int max_ctx, int split_tokens, void* stream);
+
 /* Bytes of device workspace for orthrus_argmax / orthrus_accept (0 if invalid). */
 ORTHRUS_API size_t orthrus_argmax_workspace_bytes(int rows, int vocab);
 
