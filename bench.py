@@ -427,8 +427,8 @@ def main():
         },
     }
     lm_s = op_ms["lmhead_argmax"] * 1e-3
-    if B * K <= 64:      # weight-streaming kernel: bound by one pass over the weights
-        lm_roof = {"kernel": "lmhead_rows_kernel + argmax_final_kernel (one ABI call)", "bound": "hbm",
+    if B * K <= 32:      # weight-streaming kernel: bound by one pass over the weights
+        lm_roof = {"kernel": "lmhead_kernel + argmax_final_kernel (one ABI call)", "bound": "hbm",
                    "achieved": round(lm_bytes / lm_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                    "frac": round(lm_bytes / lm_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
                    "algorithmic_bytes_per_launch": lm_bytes}

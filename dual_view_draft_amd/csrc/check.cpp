@@ -58,34 +58,21 @@ const char* status_string(int status) {
 
 int attn_split_tokens(int B, int Hkv, int max_ctx) {
   if (B < 1 || Hkv < 1 || max_ctx < 0) return kTile * 4;
-  constexpr int64_t kCUs = 256;   // one 8-wavefront workgroup fills a CU of an MI355X
-  if (B == 1) {
-    // A single sequence is cut into about one split per CU.
-    int64_t s = round_up(ceil_div(int64_t(Hkv) * (int64_t(max_ctx) + kTile), kCUs), kTile);
-    if (s < 2 * kTile) s = 2 * kTile;
-    if (s > kMaxSplitTiles * kTile) s = kMaxSplitTiles * kTile;
-    return int(s);
-  }
-  // A batch: the host knows only the longest length.  Taking the lengths as
-  // uniform on [0, max_ctx], a split of s tokens gives about
-  //   W(s) = B * Hkv * ((max_ctx / 2 + kTile / 2) / s + 1 / 2)
-  // active workgroups, which run in ceil(W / 256) rounds of one workgroup per
-  // CU, each round as long as one split.  The split with the fewest
-  // round-tokens ceil(W / 256) * s wins (the longer split on ties: fewer
-  // partial results to merge), searched over 1024 .. 4096 tokens.
-  int64_t best_s = 0, best_cost = 0;
-  for (int64_t sp = 16 * kTile; sp <= kMaxSplitTiles * kTile; sp += kTile) {
-    const double w = double(B) * Hkv * ((0.5 * max_ctx + 0.5 * kTile) / double(sp) + 0.5);
-    const int64_t cost = int64_t(std::ceil(w / double(kCUs))) * sp;
-    if (best_s == 0 || cost <= best_cost) {
-      best_s = sp;
-      best_cost = cost;
-    }
-  }
-  // a short context needs no more than one split per sequence
-  const int64_t whole = round_up(int64_t(max_ctx) + kTile, kTile);
-  if (whole < best_s) best_s = whole < 2 * kTile ? 2 * kTile : whole;
-  return int(best_s);
+  // One 8-wavefront workgroup fills a CU (256 CUs).  A single sequence is cut
+  // into about one split per CU.  A batch, whose lengths the host does not
+  // know, is cut into about four splits per CU if every sequence had the
+  // longest length (about two per CU for lengths spread evenly below it);
+  // the dispatcher starts a workgroup whenever a CU frees up, and longer
+  // splits carry the fixed cost of a split (the page-table round trip, the
+  // half merge, the partial stores, their merge) over more tokens.  On the
+  // 16-sequence ragged batch (lengths 1K-32K) splits of 3072-4096 tokens
+  // measured within 5 % of each other and 8-25 % faster than 1024-2560.
+  const int64_t work = int64_t(B) * Hkv * (int64_t(max_ctx) + kTile);
+  const int64_t target = B == 1 ? 256 : 1024;
+  int64_t s = round_up(ceil_div(work, target), kTile);
+  if (s < 2 * kTile) s = 2 * kTile;
+  if (s > kMaxSplitTiles * kTile) s = kMaxSplitTiles * kTile;
+  return int(s);
 }
 
 bool plan_attention_shape(int B, int K, int Hq, int Hkv, int D, int max_ctx, int split_tokens,
@@ -206,7 +193,9 @@ bool plan_lmhead(int rows, int hidden, int V, LmHeadPlan* p, std::string* why) {
     const int64_t narrow = ceil_div(V, kLmGemmVocabTile) * ceil_div(rows, kLmGemmRowTile);
     const int64_t wide = ceil_div(V, kLmGemmWideVocabTile) * ceil_div(rows, kLmGemmWideRowTile);
     p->gemm = ceil_div(wide, 256) * 187 < ceil_div(narrow, 256) * 100 ? 2 : 1;
-    // one row tile: contiguous vocabulary ranges, one workgroup per CU
+    // one row tile (33-128 rows): contiguous vocabulary ranges, one
+    // workgroup per CU (at 64 rows 1.3 times faster than two 32-row chunks
+    // of the streaming kernel)
     if (p->gemm == 1 && rows <= kLmGemmRowTile) p->gemm = 3;
   }
   if (p->gemm == 3) {

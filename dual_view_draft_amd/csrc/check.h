@@ -48,9 +48,8 @@ struct ArgmaxPlan {
 constexpr int kLmWorkgroups = 256;
 constexpr int kLmRowChunk = 32;
 constexpr int kLmKTile = 64;
-constexpr int kLmRegHidden = 5120;   // up to this hidden size the query rows live in registers
 
-constexpr int kLmGemmRows = 64;       // more rows than this take a GEMM-tiled kernel
+constexpr int kLmGemmRows = 32;       // more rows than this take a GEMM-tiled kernel
 constexpr int kLmGemmVocabTile = 256;
 constexpr int kLmGemmRowTile = 128;
 constexpr int kLmGemmWideVocabTile = 256;

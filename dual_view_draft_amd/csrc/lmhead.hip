@@ -200,128 +200,6 @@ __global__ __launch_bounds__(512, 1) void lmhead_kernel(LmArgs a) {
   write_row_keys(a, best, reinterpret_cast<unsigned long long*>(ring), wg, row0, wave, half, col);
 }
 
-// Row-streaming variant for hidden <= kLmRegHidden (the query rows fit in
-// registers).  A tile is 32 vocabulary rows x 512 hidden elements: every
-// weight row contributes 1 KiB of consecutive memory, fetched by one load
-// instruction (64 lanes x 16 bytes), so HBM sees long runs instead of the
-// 128-byte pieces of the tile above.  Wavefront w takes hidden elements
-// 64w .. 64w+63 of every tile; its query-row operands for all tiles are
-// loaded once into registers.  After the last tile of a block of 32
-// vocabulary rows the 8 wavefronts' partial sums meet in LDS and are added in
-// wavefront order (a fixed order: the logits do not depend on the launch).
-constexpr int R2_KT = 512;                     // hidden elements per tile
-constexpr int R2_NS = 5;                       // ring stages
-constexpr int R2_TILE = 32 * R2_KT;            // 32 KiB
-constexpr int R2_LPT = 4;                      // loads per wavefront per tile: 4 rows of 1 KiB
-constexpr int R2_MAX_KT = kLmRegHidden / R2_KT;
-
-__global__ __launch_bounds__(512, 1) void lmhead_rows_kernel(LmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ring[R2_NS * R2_TILE];
-  static_assert(8 * 32 * 32 * 4 == R2_TILE * 2, "a block's partial sums fill one stage");
-  int wg, rc;
-  lm_tile(a, &wg, &rc);
-  const int row0 = rc * RC;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, half = lane >> 5, col = lane & 31;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int v0 = int((int64_t(a.V) * wg) / a.nwg);
-  const int v1 = int((int64_t(a.V) * (wg + 1)) / a.nwg);
-  const int nkt = (a.hidden + R2_KT - 1) / R2_KT;
-  const int ntiles = ((v1 - v0 + 31) / 32) * nkt;
-
-  // query row col, hidden elements kt*512 + 64 wave + 16 ks + 8 half + 0..7
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 hreg[R2_MAX_KT][4];
-  {
-    const bool row_ok = row0 + col < a.rows;
-#pragma unroll
-    for (int kt = 0; kt < R2_MAX_KT; ++kt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int k = kt * R2_KT + wave * 64 + ks * 16 + half * 8;
-        hreg[kt][ks] = u32x4{0u, 0u, 0u, 0u};
-        if (kt < nkt && row_ok && k < a.hidden)
-          hreg[kt][ks] = *reinterpret_cast<const u32x4*>(a.h + size_t(row0 + col) * a.hidden + k);
-      }
-  }
-  wait_vmcnt<0>();                       // nothing but tile loads is in flight in the loop
-
-  // Tile t: block t / nkt, hidden tile t % nkt.  Wavefront w loads rows
-  // 4w .. 4w+3 of the block, one 1 KiB instruction each; lane l fetches
-  // granule l ^ (row % 16) so that granule c of a row sits at c ^ (row % 16).
-  auto issue_tile = [&](int t, uint16_t* st) {
-    const int blk = t / nkt;
-    const int kt = t - blk * nkt;
-    const bool live = t < ntiles;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wave * 4 + i;
-      const int v = v0 + blk * 32 + r;
-      const int c = lane ^ (r & 15);
-      const int k = kt * R2_KT + c * 8;
-      const void* src = (live && v < v1 && k < a.hidden)
-                            ? static_cast<const void*>(a.w + size_t(v) * a.hidden + k)
-                            : static_cast<const void*>(g_lm_zero16);
-      if (a.nrc == 1) load_lds16<true>(src, lds_addr(st + r * R2_KT));   // read once
-      else load_lds16(src, lds_addr(st + r * R2_KT));
-    }
-  };
-#pragma unroll
-  for (int k = 0; k < R2_NS - 1; ++k) issue_tile(k, ring + k * R2_TILE);
-
-  f32x16 acc = f32x16{};
-  unsigned long long best = 0ull;        // best key of query row col over this lane's vocabulary
-  for (int t = 0; t < ntiles; ++t) {
-    wait_vmcnt<(R2_NS - 2) * R2_LPT>();  // tile t has landed for this wavefront
-    lds_barrier();                       // ... for every wavefront; stage of t-1 is free
-    const int tn = t + R2_NS - 1;
-    issue_tile(tn, ring + (tn % R2_NS) * R2_TILE);
-    const uint16_t* wt = ring + (t % R2_NS) * R2_TILE;
-    const int blk = t / nkt;
-    const int kt = t - blk * nkt;
-#pragma unroll
-    for (int kk = 0; kk < R2_MAX_KT; ++kk) {
-      if (kk != kt) continue;            // uniform: pick this tile's register operands
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int g = wave * 8 + ks * 2 + half;   // granule of the row holding this lane's 8 elements
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(wt + col * R2_KT + ((g ^ (col & 15)) * 8));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, hreg[kk][ks]), acc, 0, 0, 0);
-      }
-    }
-    if (kt == nkt - 1) {                 // uniform: the block's partial sums are complete
-      // They meet in the stage of tile t, which no load targets before the
-      // next step's barrier.  lane l, value v: vocabulary row 8(v/4) + 4 half
-      // + v%4 of the block, query row col.
-      float* red = reinterpret_cast<float*>(ring + (t % R2_NS) * R2_TILE);
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's reads of the stage are done
-      lds_barrier();                       // ... and every other wavefront's
-#pragma unroll
-      for (int v = 0; v < 16; ++v) red[(wave * 32 + 8 * (v >> 2) + 4 * half + (v & 3)) * 32 + col] = acc[v];
-      acc = f32x16{};
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): partial sums written
-      lds_barrier();
-      // wavefront w adds up vocabulary rows 4w + 2 half + {0, 1} for query row col
-      const bool row_ok = row0 + col < a.rows;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int i = wave * 4 + 2 * half + e;
-        float sum = red[i * 32 + col];
-#pragma unroll
-        for (int w = 1; w < 8; ++w) sum += red[(w * 32 + i) * 32 + col];
-        const int vi = v0 + blk * 32 + i;
-        if (vi < v1) {
-          best = umax64(best, make_key(sum, vi));
-          if (a.logits && row_ok) a.logits[size_t(row0 + col) * a.V + vi] = sum;
-        }
-      }
-    }
-  }
-  wait_vmcnt<0>();                        // trailing zero-tile loads have landed
-  lds_barrier();                          // every wavefront is done with the ring and red
-  write_row_keys(a, best, reinterpret_cast<unsigned long long*>(ring), wg, row0, wave, half, col);
-}
-
 // GEMM-tiled variants for many query rows (batched decoding: B*K rows).
 // There the product is no longer bound by one pass over the weights: it is a
 // dense contraction (M = rows, N = vocabulary, K = hidden) whose weights
@@ -349,11 +227,11 @@ __global__ __launch_bounds__(512, 1) void lmhead_rows_kernel(LmArgs a) {
 // range mode (below).  Where several row tiles read the same weights, they
 // keep the default cache policy, which leaves them in L2 for the other row
 // tiles (the non-temporal policy cost 10 % at 512 and 768 rows).
-// Both keep one fp32 running sum per logit over 16-element products in
-// increasing hidden order, so they agree bit for bit.  The row-streaming
-// kernel instead adds eight per-wavefront partial sums, so a row's logits
-// may differ in the last bits between a call of at most 64 rows and a
-// larger one (and a near-tie may then pick another token).
+// Every LM-head kernel here keeps one fp32 running sum per logit over
+// 32x32x16 MFMA steps (A = 16 hidden elements of the weight row, B = the
+// same elements of the query row) in increasing hidden order, so a row's
+// logits are the same bits whatever kernel, tile or row count a call takes:
+// the verify pass's B*K rows and greedy decoding's B rows agree.
 template <int NWV_, int NWR_, int XB_, int YB_, int GKT_, int GNS_>
 struct GemmCfg {
   static constexpr int NWV = NWV_, NWR = NWR_, XB = XB_, YB = YB_, GKT = GKT_, GNS = GNS_;
@@ -581,7 +459,6 @@ hipError_t launch_lmhead(const LmHeadPlan& p, const void* hidden, const void* we
     return launch_kernel(&lmhead_gemm_kernel, grid, dim3(512), stream, a);
   }
   const dim3 grid(unsigned(int64_t(p.nwg) * p.nrc));
-  if (p.hidden <= kLmRegHidden) return launch_kernel(&lmhead_rows_kernel, grid, dim3(512), stream, a);
   return launch_kernel(&lmhead_kernel, grid, dim3(512), stream, a);
 }
 

@@ -212,24 +212,46 @@ __device__ int draw(ChunkW chunk_w, Weight weight, int nchunks, int chunk, int V
   if (tid == 0) { pick_s = -1; last_s = -1; }
   __syncthreads();
   // ---- level 2: which entry of chunk cstar -----------------------------------
+  // A thread's share (at most kMaxShare entries: chunks hold at most
+  // kSampleMaxChunk entries) is loaded once, its weights kept in registers
+  // for the rescan.
+  constexpr int kMaxShare = kSampleMaxChunk / kDrawThreads;
   const int v0 = cstar * chunk, v1 = min(v0 + chunk, V);
   const int per = (v1 - v0 + kDrawThreads - 1) / kDrawThreads;
   const int a0 = min(v0 + tid * per, v1), a1 = min(a0 + per, v1);
+  double wsh[kMaxShare];
+  // per is the same in every thread: the blocks of 4 past it are skipped
+  // by a uniform branch, so no masked-off exponential is issued
+#pragma unroll
+  for (int jb = 0; jb < kMaxShare; jb += 4) {
+    if (jb >= per) break;
+#pragma unroll
+    for (int j = jb; j < jb + 4; ++j) wsh[j] = a0 + j < a1 ? weight(a0 + j) : 0.0;
+  }
   double y = 0.0;
   int lastv = -1;
-  for (int v = a0; v < a1; ++v) {
-    const double wv = weight(v);
-    y += wv;
-    if (wv > 0.0) lastv = v;
+#pragma unroll
+  for (int j = 0; j < kMaxShare; ++j) {
+    if (a0 + j < a1) {
+      y += wsh[j];
+      if (wsh[j] > 0.0) lastv = a0 + j;
+    }
   }
   double e2, i2, t2;
   block_scan(y, &e2, &i2, &t2);
   if (e2 <= rem && rem < i2) {
     double cum = e2;
     int found = lastv;
-    for (int v = a0; v < a1; ++v) {
-      cum += weight(v);
-      if (cum > rem) { found = v; break; }
+    bool hit = false;
+#pragma unroll
+    for (int j = 0; j < kMaxShare; ++j) {
+      if (!hit && a0 + j < a1) {
+        cum += wsh[j];
+        if (cum > rem) {
+          found = a0 + j;
+          hit = true;
+        }
+      }
     }
     pick_s = found;
   }
@@ -240,8 +262,10 @@ __device__ int draw(ChunkW chunk_w, Weight weight, int nchunks, int chunk, int V
 }
 
 // Chunk statistics of every row: m_c and s_c = sum exp((z - m_c) / T).
+// PER entries per thread at most (chunk <= 256 PER), so that no exponential
+// is issued for entries beyond the chunk.
+template <int PER>
 __global__ __launch_bounds__(kThreads) void sample_stats_kernel(StatsArgs a) {
-  constexpr int PER = kSampleMaxChunk / kThreads;   // entries per thread at most
   __shared__ float redf[4];
   __shared__ double redd[4];
   const int row = blockIdx.y, c = blockIdx.x;
@@ -462,10 +486,17 @@ Ws carve(const SamplePlan& p, void* ws) {
             reinterpret_cast<SeqState*>(base + p.seq_off), reinterpret_cast<double*>(base + p.rs_off)};
 }
 
+hipError_t launch_stats_kernel(const SamplePlan& p, const StatsArgs& s, hipStream_t stream) {
+  const dim3 grid(p.nchunks, p.rows);
+  if (p.chunk <= 16 * kThreads) return launch_kernel(&sample_stats_kernel<16>, grid, dim3(kThreads), stream, s);
+  if (p.chunk <= 32 * kThreads) return launch_kernel(&sample_stats_kernel<32>, grid, dim3(kThreads), stream, s);
+  return launch_kernel(&sample_stats_kernel<kSampleMaxChunk / kThreads>, grid, dim3(kThreads), stream, s);
+}
+
 hipError_t launch_stats(const SamplePlan& p, const Ws& w, const float* z0, const float* z1, int rows0,
                         double inv_t, hipStream_t stream) {
   StatsArgs s{z0, z1, w.cm, w.cs, rows0, p.rows, p.V, p.chunk, p.nchunks, inv_t};
-  hipError_t e = launch_kernel(&sample_stats_kernel, dim3(p.nchunks, p.rows), dim3(kThreads), stream, s);
+  hipError_t e = launch_stats_kernel(p, s, stream);
   if (e != hipSuccess) return e;
   NormArgs n{w.cm, w.cs, w.cw, w.rn, p.rows, p.nchunks, inv_t};
   return launch_kernel(&row_norm_kernel, dim3((p.rows + 3) / 4), dim3(kThreads), stream, n);
@@ -482,7 +513,7 @@ hipError_t launch_sample(const SamplePlan& p, const float* logits, float tempera
   const double inv_t = 1.0 / double(temperature);
   if (p.nchunks <= kFusedMaxChunks) {
     StatsArgs s{logits, logits, w.cm, w.cs, p.rows, p.rows, p.V, p.chunk, p.nchunks, inv_t};
-    hipError_t e = launch_kernel(&sample_stats_kernel, dim3(p.nchunks, p.rows), dim3(kThreads), stream, s);
+    hipError_t e = launch_stats_kernel(p, s, stream);
     if (e != hipSuccess) return e;
     NormDrawArgs d{logits, u, w.cm, w.cs, out, p.V, p.chunk, p.nchunks, inv_t};
     return launch_kernel(&sample_norm_draw_kernel, dim3(p.rows), dim3(kDrawThreads), stream, d);
