@@ -278,22 +278,16 @@ bool plan_sample(int stat_rows, int B, int V, SamplePlan* p) {
   p->rows = stat_rows;
   p->B = B;
   p->V = V;
-  // about 2048 workgroups over the statistics, 4096..16384 values per chunk
-  int64_t chunk = round_up(ceil_div(int64_t(V) * (stat_rows > 0 ? stat_rows : 1), 2048), 1024);
-  if (chunk < 4096) chunk = 4096;
-  if (chunk > kSampleMaxChunk) chunk = kSampleMaxChunk;
-  if (chunk > V) chunk = V;
-  p->chunk = int(chunk);
-  p->nchunks = int(ceil_div(V, chunk));
+  p->chunk = kSampleChunk;
+  p->nchunks = int(ceil_div(V, kSampleChunk));
   p->rchunk = kResidualChunk;
   p->rchunks = B > 0 ? int(ceil_div(V, kResidualChunk)) : 0;
   const int64_t rows1 = stat_rows > 0 ? stat_rows : 1;
   const int64_t cells = rows1 * p->nchunks;
   p->cm_off = 0;
-  p->cs_off = size_t(round_up(cells * 4, 256));
+  p->cs_off = p->cm_off + size_t(round_up(cells * 4, 256));
   p->cw_off = p->cs_off + size_t(round_up(cells * 8, 256));
-  p->rn_off = p->cw_off + size_t(round_up(cells * 8, 256));
-  p->seq_off = p->rn_off + size_t(round_up(rows1 * kSampleRowBytes, 256));
+  p->seq_off = p->cw_off + size_t(round_up(cells * 8, 256));
   p->rs_off = p->seq_off + size_t(round_up(int64_t(B > 0 ? B : 1) * kSampleSeqBytes, 256));
   p->ws_bytes = p->rs_off + size_t(round_up(int64_t(B > 0 ? B : 1) * (p->rchunks > 0 ? p->rchunks : 1) * 8, 256));
   return true;
@@ -307,6 +301,8 @@ int check_sample(const float* logits, int rows, int V, float temperature, const 
   if (!(std::isfinite(temperature) && temperature > 0.f))
     return fail(err, ORTHRUS_ERR_INVALID_ARG, "temperature must be finite and > 0");
   plan_sample(rows, 0, V, plan);
+  if (int64_t(rows) * plan->nchunks > kMaxSampleCells)
+    return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "rows * ceil(vocab / 1024) must be <= 2^30");
   if (rows == 0) return ORTHRUS_OK;
   if (!logits || !u || !out) return fail(err, ORTHRUS_ERR_INVALID_ARG, "null logits/u/out");
   if (!ws || !aligned16(ws)) return fail(err, ORTHRUS_ERR_INVALID_ARG, "workspace null or misaligned");
@@ -328,6 +324,8 @@ int check_accept_sampled(const float* logits_d, const float* logits_a, const int
   if (!(std::isfinite(temperature) && temperature > 0.f))
     return fail(err, ORTHRUS_ERR_INVALID_ARG, "temperature must be finite and > 0");
   plan_sample(2 * B * K, B, V, plan);
+  if (int64_t(2 * B * K) * plan->nchunks > kMaxSampleCells)
+    return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "2 * batch * block_k * ceil(vocab / 1024) must be <= 2^30");
   if (B == 0) return ORTHRUS_OK;
   if (!logits_d || !logits_a || !draft || !u_acc || !u_res || !tokens || !n_acc || !n_emit || !next_anchor)
     return fail(err, ORTHRUS_ERR_INVALID_ARG, "null pointer argument");

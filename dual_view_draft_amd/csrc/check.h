@@ -103,15 +103,15 @@ int check_commit(const orthrus_kv* kv, int layers, int64_t pool_layer_stride, co
 // chunks of every row with statistics (m fp32, s fp64 per chunk), the
 // per-sequence acceptance state and the residual chunk sums.
 constexpr int kSampleSeqBytes = 32;
-constexpr int kSampleRowBytes = 16;
 constexpr int kResidualChunk = 1024;   // entries per residual chunk
-constexpr int kSampleMaxChunk = 16384; // entries per statistics chunk at most
+constexpr int kSampleChunk = 1024;     // entries per statistics chunk (one wavefront, 16 per lane)
+constexpr int64_t kMaxSampleCells = int64_t(1) << 30;   // statistics rows x chunks per call at most
 
 struct SamplePlan {
   int rows = 0;          // rows with chunk statistics
   int B = 0, V = 0, chunk = 0, nchunks = 0;
   int rchunk = 0, rchunks = 0;   // residual chunks (consensus only)
-  size_t cm_off = 0, cs_off = 0, cw_off = 0, rn_off = 0, seq_off = 0, rs_off = 0, ws_bytes = 0;
+  size_t cm_off = 0, cs_off = 0, cw_off = 0, seq_off = 0, rs_off = 0, ws_bytes = 0;
 };
 
 // stat_rows: rows of orthrus_sample, or 2*B*K for the consensus (B sequences).

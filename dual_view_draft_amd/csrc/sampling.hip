@@ -13,14 +13,19 @@
 // draw with a caller-supplied uniform: the smallest v whose cumulative weight
 // exceeds u times the total.
 //
-// Work layout.  Rows are cut into vocabulary chunks; a statistics pass
-// writes, per (row, chunk), the chunk's maximum logit m_c (fp32) and
-// s_c = sum exp((z - m_c) / T) (fp64); a wavefront per row then forms the
-// row maximum M, the chunk weights s_c exp((m_c - M) / T) and their sum Z in
-// a fixed order.  A draw (one 1024-thread workgroup) finds its chunk from the
-// chunk weights and then its entry inside that chunk, each time from a
-// fixed-order prefix sum over contiguous per-thread shares.  The residual of
-// a rejected row has its own, finer chunk sums.
+// Work layout.  Rows are cut into chunks of 1024 vocabulary entries; a
+// statistics pass (one wavefront per chunk, 16 entries per lane, no
+// barriers) writes, per (row, chunk), the chunk's maximum logit m_c (fp32)
+// and s_c = sum exp((z - m_c) / T) (fp64).  The next kernel forms a row's
+// maximum M, the chunk weights s_c exp((m_c - M) / T) and their sum Z in a
+// fixed order, and then draws (orthrus_sample) or runs the acceptance test
+// of a sequence's rows (consensus).  A draw (one 256-thread workgroup) finds
+// its chunk from the chunk weights and then its entry inside that chunk
+// (4 per thread), each time from a fixed-order prefix sum over contiguous
+// per-thread shares.  The residual of a rejected row has its own chunk sums.
+// (Handing the chunk results to the row's last workgroup within one launch
+// was measured slower: a device-scope fence per workgroup, or device-scope
+// atomics for the hand-over, cost more than the second launch.)
 // The exponentials and sums are fp64 so that every decision (a comparison
 // with u times a probability or a cumulative weight) agrees with an exact
 // evaluation except within about 1e-15 (relative) of its threshold.
@@ -30,13 +35,14 @@
 #include <cstdint>
 
 #include "check.h"
+#include "fexp.h"
 #include "launch.h"
 
 namespace orthrus {
 namespace {
 
-constexpr int kThreads = 256;        // statistics kernels
-constexpr int kDrawThreads = 1024;   // draw kernels (one workgroup per draw)
+constexpr int kThreads = 256;          // every sampling kernel
+constexpr int kMaxChunksInLds = 1024;  // chunk weights kept in LDS for a draw up to this many chunks
 
 struct RowNorm {       // a row's maximum and normaliser
   double Z;
@@ -60,20 +66,12 @@ struct StatsArgs {
   double inv_t;
 };
 
-struct NormArgs {
-  const float* cm;
-  const double* cs;
-  double* cw;          // [rows][nchunks]: chunk weights relative to the row maximum
-  RowNorm* rn;         // [rows]
-  int rows, nchunks;
-  double inv_t;
-};
-
 struct SampleArgs {
   const float* z;
   const float* u;      // [rows]
-  const double* cw;
-  const RowNorm* rn;
+  const float* cm;
+  const double* cs;
+  double* cw;          // [rows][nchunks], used when the weights do not fit in LDS
   int32_t* out;        // [rows]
   int V, chunk, nchunks;
   double inv_t;
@@ -84,13 +82,14 @@ struct DecideArgs {
   const float* za;     // [B*K][V] AR view
   const int32_t* draft;
   const float* u_acc;  // [B][K]
-  const RowNorm* rn;   // [2*B*K]: draft rows, then AR rows
+  const float* cm;     // statistics rows: draft rows, then AR rows
+  const double* cs;
   int32_t* tokens;     // [B][K]
   int32_t* n_acc;
   int32_t* n_emit;
   int32_t* next_anchor;
   SeqState* seq;       // [B]
-  int B, K, V;
+  int B, K, V, nchunks;
   double inv_t;
 };
 
@@ -98,8 +97,8 @@ struct ResidualArgs {
   const float* zd;
   const float* za;
   const float* u_res;  // [B][K]
-  const double* cw;    // for the fallback draw from p
-  const RowNorm* rn;
+  const float* cm;     // statistics of the AR rows, for the fallback draw from p
+  const double* cs;
   const SeqState* seq;
   double* rs;          // [B][rchunks] residual chunk sums
   int32_t* tokens;
@@ -108,8 +107,15 @@ struct ResidualArgs {
   double inv_t;
 };
 
-__device__ __forceinline__ double wexp(float z, float m, double inv_t) {
-  return exp((double(z) - double(m)) * inv_t);
+// Every kernel keeps the 2^(j/64) table of its exponential in LDS; a
+// __syncthreads must separate this from the first use.
+__device__ __forceinline__ void load_exp_table(double* tab) {
+  if (threadIdx.x < 64) tab[threadIdx.x] = kExp2Frac[threadIdx.x];
+}
+
+// exp((z - m) / T) for z <= m (every caller passes a maximum as m)
+__device__ __forceinline__ double wexp(float z, float m, double inv_t, const double* tab) {
+  return exp_nonpos((double(z) - double(m)) * inv_t, tab);
 }
 
 // Sum (or max) over a 256-thread workgroup in a fixed order: wavefront
@@ -132,13 +138,14 @@ __device__ float block_max(float x, float* red) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// Inclusive and exclusive prefix sums of one value per thread over a
-// kDrawThreads workgroup, in a fixed order (a wavefront scan, then the
-// wavefront totals in order).  incl of thread t is bitwise the excl of thread
-// t+1, so "excl <= target < incl" holds for at most one thread.
-__device__ void block_scan(double x, double* excl, double* incl, double* total) {
-  __shared__ double wsum[kDrawThreads / 64];
-  __shared__ double wpre[kDrawThreads / 64 + 1];
+// Inclusive and exclusive prefix sums of one value per thread over the
+// workgroup, in a fixed order (a wavefront scan, then the wavefront totals in
+// order), and the workgroup's maximum of one int per thread.  incl of thread
+// t is bitwise the excl of thread t+1, so "excl <= target < incl" holds for
+// at most one thread.
+__device__ void block_scan(double x, int k, double* excl, double* incl, double* total, int* kmax) {
+  __shared__ double wsum[kThreads / 64];
+  __shared__ int wmax[kThreads / 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   double v = x;
 #pragma unroll
@@ -146,41 +153,74 @@ __device__ void block_scan(double x, double* excl, double* incl, double* total) 
     const double y = __shfl_up(v, off);
     if (lane >= off) v += y;
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) k = max(k, __shfl_xor(k, off));
   double ve = __shfl_up(v, 1);
   if (lane == 0) ve = 0.0;
-  if (lane == 63) wsum[w] = v;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double run = 0.0;
-    for (int k = 0; k < kDrawThreads / 64; ++k) {
-      wpre[k] = run;
-      run = run + wsum[k];
-    }
-    wpre[kDrawThreads / 64] = run;
+  if (lane == 63) {
+    wsum[w] = v;
+    wmax[w] = k;
   }
   __syncthreads();
-  *incl = lane == 63 ? wpre[w + 1] : wpre[w] + v;
-  *excl = wpre[w] + ve;
-  *total = wpre[kDrawThreads / 64];
+  double pre[kThreads / 64 + 1];
+  pre[0] = 0.0;
+#pragma unroll
+  for (int q = 0; q < kThreads / 64; ++q) pre[q + 1] = pre[q] + wsum[q];
+  double pw = pre[0], pw1 = pre[1];
+#pragma unroll
+  for (int q = 1; q < kThreads / 64; ++q) {
+    pw = w == q ? pre[q] : pw;
+    pw1 = w == q ? pre[q + 1] : pw1;
+  }
+  *incl = lane == 63 ? pw1 : pw + v;
+  *excl = pw + ve;
+  *total = pre[kThreads / 64];
+  *kmax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
   __syncthreads();
 }
 
-// Inverse-CDF draw in one kDrawThreads workgroup over a row whose chunk
-// weights are chunk_w(c) (c < nchunks, chunks of `chunk` entries) and whose
-// entry weights are weight(v): the smallest v whose cumulative weight exceeds
-// u times the total.  Chunks, then the chosen chunk's entries, are split into
-// contiguous per-thread shares; the one thread whose share holds the target
-// rescans it in order.  If rounding leaves the target at or beyond the end
-// of a share (or of the row), the share's last entry of positive weight is
-// taken.  Every thread returns the token.
-template <class ChunkW, class Weight>
-__device__ int draw(ChunkW chunk_w, Weight weight, int nchunks, int chunk, int V, double u) {
-  __shared__ int pick_s, last_s;
+// Entries of a softmax row: weight exp((z - M) / T).
+struct SoftmaxEntry {
+  const float* z;
+  float M;
+  double inv_t;
+  const double* tab;
+  __device__ float load(int v) const { return z[v]; }
+  __device__ double weight(float zv) const { return wexp(zv, M, inv_t, tab); }
+};
+
+// Entries of a residual row: weight max(0, p - q).
+struct ResidualEntry {
+  const float* za;
+  const float* zd;
+  float Ma, Md;
+  double Za, Zd, inv_t;
+  const double* tab;
+  __device__ float2 load(int v) const { return float2{za[v], zd[v]}; }
+  __device__ double weight(float2 e) const {
+    const double p = wexp(e.x, Ma, inv_t, tab) / Za;
+    const double q = wexp(e.y, Md, inv_t, tab) / Zd;
+    return p > q ? p - q : 0.0;
+  }
+};
+
+// Inverse-CDF draw in one 256-thread workgroup over a row whose chunk
+// weights are chunk_w(c) (c < nchunks, chunks of `chunk` entries, at most
+// 256 SHARE) and whose entry weights are entry.weight(entry.load(v)): the
+// smallest v whose cumulative weight exceeds u times the total.  Chunks,
+// then the chosen chunk's entries, are split into contiguous per-thread
+// shares; the one thread whose share holds the target rescans it in order.
+// If rounding leaves the target at or beyond the end of a share (or of the
+// row), the share's last entry of positive weight is taken.  Every thread
+// returns the token.
+template <int SHARE, class ChunkW, class Entry>
+__device__ int draw(ChunkW chunk_w, const Entry& entry, int nchunks, int chunk, int V, double u) {
+  __shared__ int pick_s;
   __shared__ double rem_s;
   const int tid = threadIdx.x;
-  if (tid == 0) { pick_s = -1; last_s = -1; }
+  if (tid == 0) pick_s = -1;                       // (ordered before any write by block_scan's barrier)
   // ---- level 1: which chunk -------------------------------------------------
-  const int cpt = (nchunks + kDrawThreads - 1) / kDrawThreads;
+  const int cpt = (nchunks + kThreads - 1) / kThreads;
   const int c0 = min(tid * cpt, nchunks), c1 = min(c0 + cpt, nchunks);
   double x = 0.0;
   int lastc = -1;
@@ -190,210 +230,281 @@ __device__ int draw(ChunkW chunk_w, Weight weight, int nchunks, int chunk, int V
     if (wc > 0.0) lastc = c;
   }
   double excl, incl, total;
-  block_scan(x, &excl, &incl, &total);
+  int lastc_all;
+  block_scan(x, lastc, &excl, &incl, &total, &lastc_all);
   const double target = u * total;
   if (excl <= target && target < incl) {
     double cum = excl;
     int found = lastc;
+    double r = 0.0;
     for (int c = c0; c < c1; ++c) {
       const double before = cum;
       cum += chunk_w(c);
-      if (cum > target) { found = c; rem_s = target - before; break; }
-      if (c == lastc) rem_s = target - before;     // fallback: the share's last positive chunk
+      if (cum > target) { found = c; r = target - before; break; }
+      if (c == lastc) r = target - before;         // fallback: the share's last positive chunk
     }
     pick_s = found;
+    rem_s = r;
   }
-  if (lastc >= 0) atomicMax(&last_s, lastc);
   __syncthreads();
   int cstar = pick_s;
   double rem = rem_s;
-  if (cstar < 0) { cstar = last_s < 0 ? 0 : last_s; rem = INFINITY; }   // target beyond the row
-  __syncthreads();
-  if (tid == 0) { pick_s = -1; last_s = -1; }
-  __syncthreads();
+  if (cstar < 0) { cstar = lastc_all < 0 ? 0 : lastc_all; rem = INFINITY; }   // target beyond the row
+  __syncthreads();                                 // everyone has read pick_s
+  if (tid == 0) pick_s = -1;
   // ---- level 2: which entry of chunk cstar -----------------------------------
-  // A thread's share (at most kMaxShare entries: chunks hold at most
-  // kSampleMaxChunk entries) is loaded once, its weights kept in registers
-  // for the rescan.
-  constexpr int kMaxShare = kSampleMaxChunk / kDrawThreads;
+  // A thread's share (at most SHARE entries) is loaded at once (addresses
+  // clamped into the chunk, so that no load waits on a branch), its weights
+  // kept in registers for the rescan.  per is the same in every thread: the
+  // blocks of 4 past it are skipped by a uniform branch.
   const int v0 = cstar * chunk, v1 = min(v0 + chunk, V);
-  const int per = (v1 - v0 + kDrawThreads - 1) / kDrawThreads;
+  const int per = (v1 - v0 + kThreads - 1) / kThreads;
   const int a0 = min(v0 + tid * per, v1), a1 = min(a0 + per, v1);
-  double wsh[kMaxShare];
-  // per is the same in every thread: the blocks of 4 past it are skipped
-  // by a uniform branch, so no masked-off exponential is issued
+  decltype(entry.load(0)) raw[SHARE];
 #pragma unroll
-  for (int jb = 0; jb < kMaxShare; jb += 4) {
+  for (int jb = 0; jb < SHARE; jb += 4) {
     if (jb >= per) break;
 #pragma unroll
-    for (int j = jb; j < jb + 4; ++j) wsh[j] = a0 + j < a1 ? weight(a0 + j) : 0.0;
+    for (int j = jb; j < jb + 4; ++j) raw[j] = entry.load(min(a0 + j, v1 - 1));
   }
+  double wsh[SHARE];
   double y = 0.0;
   int lastv = -1;
 #pragma unroll
-  for (int j = 0; j < kMaxShare; ++j) {
-    if (a0 + j < a1) {
+  for (int jb = 0; jb < SHARE; jb += 4) {
+    if (jb >= per) break;
+#pragma unroll
+    for (int j = jb; j < jb + 4; ++j) {
+      const double w = entry.weight(raw[j]);       // (computed for clamped entries too: no branch)
+      wsh[j] = a0 + j < a1 ? w : 0.0;
       y += wsh[j];
       if (wsh[j] > 0.0) lastv = a0 + j;
     }
   }
   double e2, i2, t2;
-  block_scan(y, &e2, &i2, &t2);
+  int lastv_all;
+  block_scan(y, lastv, &e2, &i2, &t2, &lastv_all);
   if (e2 <= rem && rem < i2) {
     double cum = e2;
     int found = lastv;
     bool hit = false;
 #pragma unroll
-    for (int j = 0; j < kMaxShare; ++j) {
-      if (!hit && a0 + j < a1) {
-        cum += wsh[j];
-        if (cum > rem) {
-          found = a0 + j;
-          hit = true;
+    for (int jb = 0; jb < SHARE; jb += 4) {
+      if (jb >= per) break;
+#pragma unroll
+      for (int j = jb; j < jb + 4; ++j) {
+        if (!hit && a0 + j < a1) {
+          cum += wsh[j];
+          if (cum > rem) {
+            found = a0 + j;
+            hit = true;
+          }
         }
       }
     }
     pick_s = found;
   }
-  if (lastv >= 0) atomicMax(&last_s, lastv);
   __syncthreads();
-  int tok = pick_s >= 0 ? pick_s : last_s;
+  const int tok = pick_s >= 0 ? pick_s : lastv_all;
   return tok < 0 ? v0 : tok;
 }
 
-// Chunk statistics of every row: m_c and s_c = sum exp((z - m_c) / T).
-// PER entries per thread at most (chunk <= 256 PER), so that no exponential
-// is issued for entries beyond the chunk.
-template <int PER>
+// Chunk statistics of every row: m_c and s_c = sum exp((z - m_c) / T), one
+// wavefront per (row, chunk), lane l taking entries v0 + l + 64 j (j < 16).
+// The second half of them is requested only once the first half has
+// arrived, and the first half's exponentials (relative to that half's
+// maximum) run while it is in flight; the lane's two partial sums and then
+// the wavefront's are rescaled to the larger maximum (fixed butterflies).
 __global__ __launch_bounds__(kThreads) void sample_stats_kernel(StatsArgs a) {
-  __shared__ float redf[4];
-  __shared__ double redd[4];
-  const int row = blockIdx.y, c = blockIdx.x;
+  __shared__ double tab[64];
+  constexpr int PER = kSampleChunk / 64, H = PER / 2;
+  const int lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);   // row * nchunks + chunk
+  const bool live = unit < a.rows * a.nchunks;     // (at most 2^30 units)
+  const int row = live ? unit / a.nchunks : 0;
+  const int c = live ? unit - row * a.nchunks : 0;
   const float* z = row < a.rows0 ? a.z0 + size_t(row) * a.V : a.z1 + size_t(row - a.rows0) * a.V;
-  const int v0 = c * a.chunk, v1 = min(v0 + a.chunk, a.V);
-  // thread t's entries v0 + t + 256 j, all loaded at once and kept in registers
+  const int v0 = c * kSampleChunk, v1 = live ? min(v0 + kSampleChunk, a.V) : v0;
+  const int vt = v0 + lane;
   float x[PER];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int v = v0 + threadIdx.x + j * kThreads;
-    x[j] = v < v1 ? z[v] : -INFINITY;
-  }
-  float m = -INFINITY;
+  for (int j = 0; j < H; ++j) x[j] = vt + j * 64 < v1 ? z[vt + j * 64] : -INFINITY;
+  load_exp_table(tab);
+  __syncthreads();
+  if (!live) return;                               // uniform per wavefront, after the only barrier
+  // the second half's addresses wait on the first half's data
+  int vb = vt;
+  asm volatile("" : "+v"(vb) : "v"(x[H - 1]));
 #pragma unroll
-  for (int j = 0; j < PER; ++j) m = fmaxf(m, x[j]);
-  m = block_max(m, redf);
-  double s = 0.0;                                  // in increasing v, as the entries were read
+  for (int j = H; j < PER; ++j) x[j] = vt + j * 64 < v1 ? z[vb + j * 64] : -INFINITY;
+  // Entries past the chunk hold -inf and add exp(-inf) = +0 exactly (no
+  // branch per entry); a half with no entries at all has m = -inf, and its
+  // NaN sum is replaced by 0.
+  const double inv_t = a.inv_t;
+  float m1 = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if (v0 + int(threadIdx.x) + j * kThreads < v1) s += wexp(x[j], m, a.inv_t);
-  s = block_sum(s, redd);
-  if (threadIdx.x == 0) {
+  for (int j = 0; j < H; ++j) m1 = fmaxf(m1, x[j]);
+  double s1 = 0.0;                                 // in increasing v, as the entries were read
+#pragma unroll
+  for (int j = 0; j < H; ++j) s1 += wexp(x[j], m1, inv_t, tab);
+  s1 = m1 == -INFINITY ? 0.0 : s1;
+  float m2 = m1;
+#pragma unroll
+  for (int j = H; j < PER; ++j) m2 = fmaxf(m2, x[j]);
+  double s2 = 0.0;
+#pragma unroll
+  for (int j = H; j < PER; ++j) s2 += wexp(x[j], m2, inv_t, tab);
+  s2 = m2 == -INFINITY ? 0.0 : s2;
+  double sl = (m1 == m2 ? s1 : s1 * wexp(m1, m2, inv_t, tab)) + s2;   // the lane's sum relative to m2
+  float m = m2;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  double sw = m2 == m ? sl : sl * wexp(m2, m, inv_t, tab);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sw += __shfl_xor(sw, off);
+  if (lane == 0) {
     a.cm[size_t(row) * a.nchunks + c] = m;
-    a.cs[size_t(row) * a.nchunks + c] = s;
+    a.cs[size_t(row) * a.nchunks + c] = sw;
   }
 }
 
-// One wavefront per row: the row maximum M, every chunk's weight
-// s_c exp((m_c - M) / T) and their sum Z (lane-strided, then a fixed butterfly).
-__global__ __launch_bounds__(kThreads) void row_norm_kernel(NormArgs a) {
-  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (row >= a.rows) return;                       // uniform per wavefront
-  const int lane = threadIdx.x & 63;
+// One workgroup per row: the row maximum M, every chunk's weight
+// s_c exp((m_c - M) / T) (into LDS, or global memory past kMaxChunksInLds
+// chunks), then out[row] = draw of softmax(z[row] / T) with u[row].
+__global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a) {
+  __shared__ float redf[4];
+  __shared__ double tab[64];
+  __shared__ double cw_s[kMaxChunksInLds];
+  const int row = blockIdx.x;
   const float* cm = a.cm + size_t(row) * a.nchunks;
   const double* cs = a.cs + size_t(row) * a.nchunks;
   double* cw = a.cw + size_t(row) * a.nchunks;
-  float m = -INFINITY;
-  for (int c = lane; c < a.nchunks; c += 64) m = fmaxf(m, cm[c]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  double z = 0.0;
-  for (int c = lane; c < a.nchunks; c += 64) {
-    const double w = cs[c] * wexp(cm[c], m, a.inv_t);
-    cw[c] = w;
-    z += w;
+  // every independent load first: the thread's first chunk, the uniform,
+  // the exponential's table
+  const int k0 = threadIdx.x;
+  const float cm0 = k0 < a.nchunks ? cm[k0] : -INFINITY;
+  const double cs0 = k0 < a.nchunks ? cs[k0] : 0.0;
+  const double u = double(a.u[row]);
+  load_exp_table(tab);
+  float M = cm0;
+  for (int k = k0 + kThreads; k < a.nchunks; k += kThreads) M = fmaxf(M, cm[k]);
+  M = block_max(M, redf);                          // (its barriers also publish the table)
+  const bool in_lds = a.nchunks <= kMaxChunksInLds;
+  if (k0 < a.nchunks) {
+    const double w = cs0 * wexp(cm0, M, a.inv_t, tab);
+    if (in_lds) cw_s[k0] = w;
+    else cw[k0] = w;
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
-  if (lane == 0) a.rn[row] = RowNorm{z, m, 0};
-}
-
-// One workgroup per row: out[row] = draw of softmax(z[row] / T) with u[row].
-__global__ __launch_bounds__(kDrawThreads) void sample_draw_kernel(SampleArgs a) {
-  const int row = blockIdx.x;
-  const double* cw = a.cw + size_t(row) * a.nchunks;
-  const float M = a.rn[row].M;
-  const float* z = a.z + size_t(row) * a.V;
-  const double inv_t = a.inv_t;
-  const int tok = draw([&](int c) { return cw[c]; }, [&](int v) { return wexp(z[v], M, inv_t); },
-                       a.nchunks, a.chunk, a.V, double(a.u[row]));
-  if (threadIdx.x == 0) a.out[row] = tok;
-}
-
-// Draw with the row's normalisation done in the same workgroup: wavefront 0
-// forms M, the chunk weights and Z exactly as row_norm_kernel does (the same
-// lane-strided order and butterfly), into LDS; then the draw as in
-// sample_draw_kernel.  One launch fewer for orthrus_sample, whose rows need
-// no normaliser afterwards.
-constexpr int kFusedMaxChunks = 1024;
-
-struct NormDrawArgs {
-  const float* z;
-  const float* u;      // [rows]
-  const float* cm;     // [rows][nchunks]
-  const double* cs;
-  int32_t* out;        // [rows]
-  int V, chunk, nchunks;
-  double inv_t;
-};
-
-__global__ __launch_bounds__(kDrawThreads) void sample_norm_draw_kernel(NormDrawArgs a) {
-  __shared__ double cw_s[kFusedMaxChunks];
-  __shared__ float m_s;
-  const int row = blockIdx.x;
-  if (threadIdx.x < 64) {                          // wavefront 0: row_norm_kernel's steps
-    const int lane = threadIdx.x;
-    const float* cm = a.cm + size_t(row) * a.nchunks;
-    const double* cs = a.cs + size_t(row) * a.nchunks;
-    float m = -INFINITY;
-    for (int c = lane; c < a.nchunks; c += 64) m = fmaxf(m, cm[c]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    for (int c = lane; c < a.nchunks; c += 64) cw_s[c] = cs[c] * wexp(cm[c], m, a.inv_t);
-    if (lane == 0) m_s = m;
+  for (int k = k0 + kThreads; k < a.nchunks; k += kThreads) {
+    const double w = cs[k] * wexp(cm[k], M, a.inv_t, tab);
+    if (in_lds) cw_s[k] = w;
+    else cw[k] = w;
   }
   __syncthreads();
-  const float M = m_s;
-  const float* z = a.z + size_t(row) * a.V;
-  const double inv_t = a.inv_t;
-  const int tok = draw([&](int c) { return cw_s[c]; }, [&](int v) { return wexp(z[v], M, inv_t); },
-                       a.nchunks, a.chunk, a.V, double(a.u[row]));
+  const int tok = draw<kSampleChunk / kThreads>([&](int k) { return in_lds ? cw_s[k] : cw[k]; },
+                              SoftmaxEntry{a.z + size_t(row) * a.V, M, a.inv_t, tab}, a.nchunks, a.chunk, a.V, u);
   if (threadIdx.x == 0) a.out[row] = tok;
 }
 
-// One wavefront per sequence, lane i = block row i: the acceptance test of
-// every row, then the first rejection.
-__global__ __launch_bounds__(64) void sample_decide_kernel(DecideArgs a) {
+// One workgroup per sequence: the maximum and normaliser of each of its 2K
+// statistics rows (a group of G threads per row, chunks strided over the
+// group, then a butterfly within the group), then wavefront 0, lane i = block
+// row i, runs the acceptance test of every row and finds the first
+// rejection.
+constexpr int kDecideThreads = 1024;
+
+__global__ __launch_bounds__(kDecideThreads) void sample_decide_kernel(DecideArgs a) {
+  __shared__ double tab[64];
+  __shared__ RowNorm rn_s[2 * ORTHRUS_MAX_BLOCK];
+  constexpr int kReg = 16;                         // chunks per thread per batch of loads
   const int b = blockIdx.x;
+  const int BK = a.B * a.K, R = 2 * a.K;
+  // the table first, so that waiting for it does not wait for the loads below
+  const double tab_v = threadIdx.x < 64 ? kExp2Frac[threadIdx.x] : 0.0;
+  int G = 64;                                      // threads per row: a power of two, G * R <= 1024
+  while (G * R > kDecideThreads) G >>= 1;
+  const int r = threadIdx.x / G, gl = threadIdx.x % G;
+  const bool has_row = r < R;                      // whole groups: G divides 64
+  const size_t srow = (r < a.K ? size_t(b) * a.K + r : size_t(BK) + size_t(b) * a.K + (r - a.K));
+  const float* cm = a.cm + (has_row ? srow : 0) * a.nchunks;
+  const double* cs = a.cs + (has_row ? srow : 0) * a.nchunks;
+  // every independent load first: the rows' first batch of statistics, and
+  // for wavefront 0 (lane i = block row i) the drafted token, its uniform
+  // and its logits
   const int i = threadIdx.x;
-  const int BK = a.B * a.K;
-  bool reject = false;
-  int32_t t = 0;
-  RowNorm nd{0.0, 0.f, 0}, na{0.0, 0.f, 0};
-  if (i < a.K) {
-    const size_t rd = size_t(b) * a.K + i;
-    nd = a.rn[rd];
-    na = a.rn[BK + rd];
-    t = a.draft[rd];
-    double p = 0.0, q = 0.0;                       // a token outside the vocabulary has p = q = 0
-    if (t >= 0 && t < a.V) {
-      p = wexp(a.za[rd * a.V + t], na.M, a.inv_t) / na.Z;
-      q = wexp(a.zd[rd * a.V + t], nd.M, a.inv_t) / nd.Z;
+  const bool lane_row = i < a.K;
+  const size_t rd = size_t(b) * a.K + (lane_row ? i : 0);
+  const int32_t t = a.draft[rd];                   // (rd is a valid row for every lane: no branch)
+  const float uacc = a.u_acc[rd];
+  float mv[kReg];
+  double sv[kReg];
+#pragma unroll
+  for (int q = 0; q < kReg; ++q) {
+    const int k = gl + q * G;
+    const bool ok = has_row && k < a.nchunks;
+    mv[q] = ok ? cm[k] : -INFINITY;
+    sv[q] = ok ? cs[k] : 0.0;
+  }
+  const bool in_vocab = lane_row && t >= 0 && t < a.V;
+  const float zta = in_vocab ? a.za[rd * a.V + t] : 0.f;
+  const float ztd = in_vocab ? a.zd[rd * a.V + t] : 0.f;
+  if (threadIdx.x < 64) tab[threadIdx.x] = tab_v;
+  __syncthreads();
+  if (has_row) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kReg; ++q) m = fmaxf(m, mv[q]);
+    for (int k0 = gl + kReg * G; k0 < a.nchunks; k0 += kReg * G) {   // further batches (large vocabularies)
+      float mb[kReg];
+#pragma unroll
+      for (int q = 0; q < kReg; ++q) mb[q] = k0 + q * G < a.nchunks ? cm[k0 + q * G] : -INFINITY;
+#pragma unroll
+      for (int q = 0; q < kReg; ++q) m = fmaxf(m, mb[q]);
     }
-    reject = !(double(a.u_acc[rd]) * q < p);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+      if (off < G) m = fmaxf(m, __shfl_xor(m, off));   // within the group: G is uniform
+    double zs = 0.0;
+#pragma unroll
+    for (int q = 0; q < kReg; ++q)
+      if (gl + q * G < a.nchunks) zs += sv[q] * wexp(mv[q], m, a.inv_t, tab);   // uniform but for the last
+    for (int k0 = gl + kReg * G; k0 < a.nchunks; k0 += kReg * G) {
+      float mb[kReg];
+      double sb[kReg];
+#pragma unroll
+      for (int q = 0; q < kReg; ++q) {
+        const bool ok = k0 + q * G < a.nchunks;
+        mb[q] = ok ? cm[k0 + q * G] : -INFINITY;
+        sb[q] = ok ? cs[k0 + q * G] : 0.0;
+      }
+#pragma unroll
+      for (int q = 0; q < kReg; ++q) {
+        const double w = sb[q] * wexp(mb[q], m, a.inv_t, tab);
+        zs += k0 + q * G < a.nchunks ? w : 0.0;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+      if (off < G) zs += __shfl_xor(zs, off);
+    if (gl == 0) rn_s[r] = RowNorm{zs, m, 0};
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  bool reject = false;
+  RowNorm nd{0.0, 0.f, 0}, na{0.0, 0.f, 0};
+  if (lane_row) {
+    nd = rn_s[i];
+    na = rn_s[a.K + i];
+    double p = 0.0, q = 0.0;                       // a token outside the vocabulary has p = q = 0
+    if (in_vocab) {
+      p = wexp(zta, na.M, a.inv_t, tab) / na.Z;
+      q = wexp(ztd, nd.M, a.inv_t, tab) / nd.Z;
+    }
+    reject = !(double(uacc) * q < p);
   }
   const unsigned long long bad = __ballot(reject);
   const int j = bad ? (__ffsll(static_cast<long long>(bad)) - 1) : a.K;
-  if (i < a.K) a.tokens[size_t(b) * a.K + i] = i < j ? t : -1;
+  if (lane_row) a.tokens[size_t(b) * a.K + i] = i < j ? t : -1;
   if (i == 0) {
     a.n_acc[b] = j;
     a.n_emit[b] = j < a.K ? j + 1 : a.K;
@@ -405,30 +516,21 @@ __global__ __launch_bounds__(64) void sample_decide_kernel(DecideArgs a) {
   if (i == j) a.seq[b] = SeqState{na.Z, nd.Z, na.M, nd.M, j, 0};
 }
 
-struct Residual {
-  const float* za;
-  const float* zd;
-  float Ma, Md;
-  double Za, Zd, inv_t;
-  __device__ double operator()(int v) const {
-    const double p = wexp(za[v], Ma, inv_t) / Za;
-    const double q = wexp(zd[v], Md, inv_t) / Zd;
-    return p > q ? p - q : 0.0;
-  }
-};
-
 // Sums of the residual max(0, p - q) of each sequence's rejected row over
 // chunks of rchunk entries.
 __global__ __launch_bounds__(kThreads) void residual_stats_kernel(ResidualArgs a) {
   __shared__ double redd[4];
+  __shared__ double tab[64];
   const int b = blockIdx.y, c = blockIdx.x;
   const SeqState st = a.seq[b];
   if (st.j >= a.K) return;                         // uniform: nothing rejected
+  load_exp_table(tab);
+  __syncthreads();
   const size_t row = size_t(b) * a.K + st.j;
-  const Residual r{a.za + row * a.V, a.zd + row * a.V, st.Ma, st.Md, st.Za, st.Zd, a.inv_t};
+  const ResidualEntry r{a.za + row * a.V, a.zd + row * a.V, st.Ma, st.Md, st.Za, st.Zd, a.inv_t, tab};
   const int v0 = c * a.rchunk, v1 = min(v0 + a.rchunk, a.V);
   double s = 0.0;
-  for (int v = v0 + threadIdx.x; v < v1; v += kThreads) s += r(v);
+  for (int v = v0 + threadIdx.x; v < v1; v += kThreads) s += r.weight(r.load(v));
   s = block_sum(s, redd);
   if (threadIdx.x == 0) a.rs[size_t(b) * a.rchunks + c] = s;
 }
@@ -436,33 +538,42 @@ __global__ __launch_bounds__(kThreads) void residual_stats_kernel(ResidualArgs a
 // One workgroup per sequence: the emitted token at the rejected row, a draw
 // of max(0, p - q) (of p if the residual is empty, which only rounding can
 // cause).
-__global__ __launch_bounds__(kDrawThreads) void residual_draw_kernel(ResidualArgs a) {
+__global__ __launch_bounds__(kThreads) void residual_draw_kernel(ResidualArgs a) {
+  __shared__ double tab[64];
+  __shared__ double rs_s[kMaxChunksInLds];
+  __shared__ float u_s[ORTHRUS_MAX_BLOCK];
   const int b = blockIdx.x;
+  // every independent load first: the sequence's state, its residual chunk
+  // sums (into LDS when they fit), the uniforms of all its rows
   const SeqState st = a.seq[b];
-  if (st.j >= a.K) return;
-  const size_t row = size_t(b) * a.K + st.j;
   const double* rs = a.rs + size_t(b) * a.rchunks;
-  __shared__ double part[kDrawThreads / 64];
-  double x = 0.0;
-  for (int c = threadIdx.x; c < a.rchunks; c += kDrawThreads) x += rs[c];
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
-  __syncthreads();
-  bool empty = true;
-  for (int k = 0; k < kDrawThreads / 64; ++k) empty = empty && !(part[k] > 0.0);
-  const double u = double(a.u_res[row]);
+  const bool in_lds = a.rchunks <= kMaxChunksInLds;
+  bool pos = false;
+  for (int k = threadIdx.x; k < a.rchunks; k += kThreads) {
+    const double w = rs[k];
+    if (in_lds) rs_s[k] = w;
+    pos = pos || w > 0.0;
+  }
+  if (threadIdx.x < a.K) u_s[threadIdx.x] = a.u_res[size_t(b) * a.K + threadIdx.x];
+  load_exp_table(tab);
+  if (st.j >= a.K) return;                         // uniform: nothing rejected
+  const bool nonempty = __syncthreads_or(pos);     // (also publishes the LDS copies)
+  const size_t row = size_t(b) * a.K + st.j;
+  const double u = double(u_s[st.j]);
   int tok;
-  if (!empty) {
-    const Residual r{a.za + row * a.V, a.zd + row * a.V, st.Ma, st.Md, st.Za, st.Zd, a.inv_t};
-    tok = draw([&](int c) { return rs[c]; }, r, a.rchunks, a.rchunk, a.V, u);
+  if (nonempty) {
+    const ResidualEntry r{a.za + row * a.V, a.zd + row * a.V, st.Ma, st.Md, st.Za, st.Zd, a.inv_t, tab};
+    tok = draw<kResidualChunk / kThreads>([&](int k) { return in_lds ? rs_s[k] : rs[k]; }, r, a.rchunks,
+                                          a.rchunk, a.V, u);
   } else {
-    const double* cw = a.cw + (size_t(a.B) * a.K + row) * a.nchunks;
-    const float* z = a.za + row * a.V;
+    const size_t srow = size_t(a.B) * a.K + row;   // the AR view's statistics row
+    const float* cm = a.cm + srow * a.nchunks;
+    const double* cs = a.cs + srow * a.nchunks;
     const float M = st.Ma;
     const double inv_t = a.inv_t;
-    tok = draw([&](int c) { return cw[c]; }, [&](int v) { return wexp(z[v], M, inv_t); },
-               a.nchunks, a.chunk, a.V, u);
+    tok = draw<kSampleChunk / kThreads>([&](int k) { return cs[k] * wexp(cm[k], M, inv_t, tab); },
+                                           SoftmaxEntry{a.za + row * a.V, M, inv_t, tab}, a.nchunks, a.chunk, a.V,
+                                           u);
   }
   if (threadIdx.x == 0) {
     a.tokens[row] = tok;
@@ -474,7 +585,6 @@ struct Ws {
   float* cm;
   double* cs;
   double* cw;
-  RowNorm* rn;
   SeqState* seq;
   double* rs;
 };
@@ -482,46 +592,31 @@ struct Ws {
 Ws carve(const SamplePlan& p, void* ws) {
   char* base = static_cast<char*>(ws);
   return Ws{reinterpret_cast<float*>(base + p.cm_off), reinterpret_cast<double*>(base + p.cs_off),
-            reinterpret_cast<double*>(base + p.cw_off), reinterpret_cast<RowNorm*>(base + p.rn_off),
-            reinterpret_cast<SeqState*>(base + p.seq_off), reinterpret_cast<double*>(base + p.rs_off)};
+            reinterpret_cast<double*>(base + p.cw_off), reinterpret_cast<SeqState*>(base + p.seq_off),
+            reinterpret_cast<double*>(base + p.rs_off)};
 }
 
-hipError_t launch_stats_kernel(const SamplePlan& p, const StatsArgs& s, hipStream_t stream) {
-  const dim3 grid(p.nchunks, p.rows);
-  if (p.chunk <= 16 * kThreads) return launch_kernel(&sample_stats_kernel<16>, grid, dim3(kThreads), stream, s);
-  if (p.chunk <= 32 * kThreads) return launch_kernel(&sample_stats_kernel<32>, grid, dim3(kThreads), stream, s);
-  return launch_kernel(&sample_stats_kernel<kSampleMaxChunk / kThreads>, grid, dim3(kThreads), stream, s);
-}
-
-hipError_t launch_stats(const SamplePlan& p, const Ws& w, const float* z0, const float* z1, int rows0,
-                        double inv_t, hipStream_t stream) {
-  StatsArgs s{z0, z1, w.cm, w.cs, rows0, p.rows, p.V, p.chunk, p.nchunks, inv_t};
-  hipError_t e = launch_stats_kernel(p, s, stream);
-  if (e != hipSuccess) return e;
-  NormArgs n{w.cm, w.cs, w.cw, w.rn, p.rows, p.nchunks, inv_t};
-  return launch_kernel(&row_norm_kernel, dim3((p.rows + 3) / 4), dim3(kThreads), stream, n);
+hipError_t launch_stats(const SamplePlan& p, const StatsArgs& s, hipStream_t stream) {
+  const int64_t units = int64_t(p.rows) * p.nchunks;
+  const dim3 grid(unsigned((units + kThreads / 64 - 1) / (kThreads / 64)));
+  return launch_kernel(&sample_stats_kernel, grid, dim3(kThreads), stream, s);
 }
 
 }  // namespace
 
 static_assert(sizeof(SeqState) == kSampleSeqBytes, "per-sequence state size");
-static_assert(sizeof(RowNorm) == kSampleRowBytes, "per-row state size");
+static_assert(kResidualChunk % (4 * kThreads) == 0 && kSampleChunk == 64 * 16 && kSampleChunk % (4 * kThreads) == 0,
+              "chunk shares");
 
 hipError_t launch_sample(const SamplePlan& p, const float* logits, float temperature, const float* u,
                          int32_t* out, void* ws, hipStream_t stream) {
   const Ws w = carve(p, ws);
   const double inv_t = 1.0 / double(temperature);
-  if (p.nchunks <= kFusedMaxChunks) {
-    StatsArgs s{logits, logits, w.cm, w.cs, p.rows, p.rows, p.V, p.chunk, p.nchunks, inv_t};
-    hipError_t e = launch_stats_kernel(p, s, stream);
-    if (e != hipSuccess) return e;
-    NormDrawArgs d{logits, u, w.cm, w.cs, out, p.V, p.chunk, p.nchunks, inv_t};
-    return launch_kernel(&sample_norm_draw_kernel, dim3(p.rows), dim3(kDrawThreads), stream, d);
-  }
-  hipError_t e = launch_stats(p, w, logits, logits, p.rows, inv_t, stream);
+  hipError_t e = launch_stats(p, StatsArgs{logits, logits, w.cm, w.cs, p.rows, p.rows, p.V, p.chunk, p.nchunks,
+                                           inv_t}, stream);
   if (e != hipSuccess) return e;
-  SampleArgs d{logits, u, w.cw, w.rn, out, p.V, p.chunk, p.nchunks, inv_t};
-  return launch_kernel(&sample_draw_kernel, dim3(p.rows), dim3(kDrawThreads), stream, d);
+  const SampleArgs d{logits, u, w.cm, w.cs, w.cw, out, p.V, p.chunk, p.nchunks, inv_t};
+  return launch_kernel(&sample_draw_kernel, dim3(p.rows), dim3(kThreads), stream, d);
 }
 
 hipError_t launch_accept_sampled(const SamplePlan& p, const float* logits_d, const float* logits_a,
@@ -530,17 +625,18 @@ hipError_t launch_accept_sampled(const SamplePlan& p, const float* logits_d, con
                                  int32_t* next_anchor, void* ws, hipStream_t stream) {
   const Ws w = carve(p, ws);
   const double inv_t = 1.0 / double(temperature);
-  hipError_t e = launch_stats(p, w, logits_d, logits_a, B * K, inv_t, stream);
+  hipError_t e = launch_stats(p, StatsArgs{logits_d, logits_a, w.cm, w.cs, B * K, p.rows, p.V, p.chunk,
+                                           p.nchunks, inv_t}, stream);
   if (e != hipSuccess) return e;
-  DecideArgs d{logits_d, logits_a, draft, u_acc, w.rn, tokens, n_acc, n_emit, next_anchor, w.seq,
-               B, K, p.V, inv_t};
-  e = launch_kernel(&sample_decide_kernel, dim3(B), dim3(64), stream, d);
+  const DecideArgs d{logits_d, logits_a, draft, u_acc, w.cm, w.cs, tokens, n_acc, n_emit, next_anchor, w.seq,
+                     B, K, p.V, p.nchunks, inv_t};
+  e = launch_kernel(&sample_decide_kernel, dim3(B), dim3(kDecideThreads), stream, d);
   if (e != hipSuccess) return e;
-  ResidualArgs r{logits_d, logits_a, u_res, w.cw, w.rn, w.seq, w.rs, tokens, next_anchor,
-                 B, K, p.V, p.chunk, p.nchunks, p.rchunk, p.rchunks, inv_t};
+  const ResidualArgs r{logits_d, logits_a, u_res, w.cm, w.cs, w.seq, w.rs, tokens, next_anchor,
+                       B, K, p.V, p.chunk, p.nchunks, p.rchunk, p.rchunks, inv_t};
   e = launch_kernel(&residual_stats_kernel, dim3(p.rchunks, B), dim3(kThreads), stream, r);
   if (e != hipSuccess) return e;
-  return launch_kernel(&residual_draw_kernel, dim3(B), dim3(kDrawThreads), stream, r);
+  return launch_kernel(&residual_draw_kernel, dim3(B), dim3(kThreads), stream, r);
 }
 
 }  // namespace orthrus

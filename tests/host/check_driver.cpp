@@ -1,3 +1,5 @@
+#include <algorithm>
+#include <cmath>
 // Host-only driver for the C-ABI argument checks (built with g++ and the
 // address/undefined-behaviour sanitizers by tests/test_abi_cpu.py; no HIP).
 #include <cstdio>
@@ -5,6 +7,7 @@
 #include <string>
 
 #include "check.h"
+#include "fexp.h"
 
 static int failures = 0;
 #define EXPECT(cond)                                                  \
@@ -86,12 +89,17 @@ int main() {
   EXPECT(plan_lmhead(300, 1024, 20011, &lp, nullptr) && lp.gemm == 1);
   EXPECT(!plan_lmhead(32, 4000, 151936, &lp, nullptr));   // hidden not a multiple of 64
 
-  // sampling statistics: chunks of 4096..16384 entries; 1 x 4.2 M words makes
-  // 1026 chunks (more than the fused draw's 1024)
+  // sampling statistics: chunks of 1024 entries; 4.2 M words make 4102
+  // chunks (more than the 1024 whose weights a draw keeps in LDS)
   SamplePlan sp;
-  EXPECT(plan_sample(32, 0, 151936, &sp) && sp.chunk == 4096 && sp.nchunks == 38);
-  EXPECT(plan_sample(1, 0, 4200000, &sp) && sp.chunk == 4096 && sp.nchunks == 1026);
-  EXPECT(plan_sample(2, 0, 4200000, &sp) && sp.chunk <= kSampleMaxChunk && sp.nchunks <= 1024);
+  EXPECT(plan_sample(32, 0, 151936, &sp) && sp.chunk == 1024 && sp.nchunks == 149);
+  EXPECT(plan_sample(2 * 16 * 32, 16, 151936, &sp) && sp.nchunks == 149 && sp.rchunks == 149);
+  EXPECT(sp.cs_off >= size_t(1024) * 149 * 4 && sp.rs_off + size_t(16) * sp.rchunks * 8 <= sp.ws_bytes);
+  EXPECT(plan_sample(1, 0, 4200000, &sp) && sp.nchunks == 4102);
+  EXPECT(plan_sample(7, 0, 1000, &sp) && sp.nchunks == 1);
+  // at most 2^30 (row, chunk) cells per call
+  EXPECT(check_sample(reinterpret_cast<const float*>(P), 65535, 1 << 26, 1.0f, reinterpret_cast<const float*>(P), I, P, size_t(1) << 50, &sp, &err) == ORTHRUS_ERR_UNSUPPORTED_SHAPE);
+  EXPECT(check_sample(reinterpret_cast<const float*>(P), 1024, 1 << 20, 1.0f, reinterpret_cast<const float*>(P), I, P, size_t(1) << 50, &sp, &err) == ORTHRUS_OK);
   EXPECT(check_sample(reinterpret_cast<const float*>(P), 1, kMaxVocab + 1, 1.0f, reinterpret_cast<const float*>(P), I, P, size_t(1) << 40, &sp, &err) == ORTHRUS_ERR_UNSUPPORTED_SHAPE);
   EXPECT(check_accept_sampled(reinterpret_cast<const float*>(P), reinterpret_cast<const float*>(P), I, 1, 32, kMaxVocab + 1, 1.0f, reinterpret_cast<const float*>(P), reinterpret_cast<const float*>(P), I, I, I, I, P, size_t(1) << 40, &sp, &err) == ORTHRUS_ERR_UNSUPPORTED_SHAPE);
 
@@ -103,6 +111,37 @@ int main() {
   EXPECT(check_commit(&kv, 0, 0, P, P, 0, I, 1, 32, O, &err) == ORTHRUS_ERR_INVALID_ARG);
 
   for (int s : {0, -1, -2, -3, -4, -5, -99}) EXPECT(std::string(status_string(s)).rfind("ORTHRUS_", 0) == 0);
+
+  // the sampling kernels' exp for x <= 0: within 2 ulp of the C library's
+  // exp on a dense grid of [-760, 0] plus landmarks (0, the table and
+  // reduction boundaries, the underflow region), exactly 0 far below; and
+  // the table is 2^(j/64) to within half an ulp of the library's exp2
+  {
+    for (int j = 0; j < 64; ++j) {
+      const double want = std::exp2(j / 64.0);
+      EXPECT(std::fabs(kExp2Frac[j] - want) <= 0.5 * (std::nextafter(want, 4.0) - want));
+    }
+    double worst = 0.0;
+    auto check = [&](double x) {
+      const double got = exp_nonpos(x, kExp2Frac), want = std::exp(x);
+      if (want < 0x1p-1022) { EXPECT(std::fabs(got - want) <= 0x1p-1070); return; }
+      const double ulp = std::nextafter(want, 1e300) - want;
+      worst = std::max(worst, std::fabs(got - want) / ulp);
+    };
+    for (int i = 0; i <= 4000000; ++i) check(-760.0 * i / 4000000.0);
+    for (int n = -2000; n <= 0; ++n) {           // around every reduction boundary (n + 1/2) ln2 / 64
+      const double b = (n + 0.5) * 0.6931471805599453 / 64;
+      check(b);
+      check(std::nextafter(b, 0.0));
+      check(std::nextafter(b, -1.0));
+    }
+    for (double x : {0.0, -0.0, -1e-300, -1e-17, -708.3, -708.4, -745.1, -745.2, -750.0})
+      check(x);
+    EXPECT(exp_nonpos(-1e30, kExp2Frac) == 0.0 && exp_nonpos(-800.0, kExp2Frac) == 0.0);
+    EXPECT(exp_nonpos(0.0, kExp2Frac) == 1.0);
+    EXPECT(worst <= 2.0);
+    std::printf("exp_nonpos: worst %.2f ulp\n", worst);
+  }
   std::printf("%s (%d failures)\n", failures ? "FAIL" : "OK", failures);
   return failures ? 1 : 0;
 }

@@ -41,8 +41,8 @@ def uniforms(rng, shape):
     return rng.random(shape, dtype=np.float32)    # float32 in [0, 1)
 
 
-# 1 x 4.2 M words: more than 1024 statistics chunks per row, so the draw takes
-# the separate normalisation kernel instead of forming the weights itself
+# 1 x 4.2 M words: more than 1024 statistics chunks per row, so the draw reads
+# the chunk weights from global memory instead of LDS
 @pytest.mark.parametrize("rows,V,T", [(32, 151936, 1.0), (32, 151936, 0.6), (7, 1000, 2.5), (1, 1, 1.0),
                                       (65, 5000, 0.3), (3, 20000, 1.0), (1, 4200000, 0.8)])
 def test_sample_matches_oracle(lib, rows, V, T):
@@ -57,6 +57,44 @@ def test_sample_matches_oracle(lib, rows, V, T):
     lib.orthrus_sample(f32_dev(z), T, f32_dev(u), out)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), sample_rows(z, T, u))
+
+
+def test_one_workspace_serves_calls_in_a_row(lib):
+    """One workspace, never cleared, serves calls of different shapes one
+    after another, for both entry points (garbage from the previous call is
+    never read)."""
+    from oracle.sampling import sample_rows, speculative_accept
+    rng = np.random.default_rng(21)
+    shapes = ((32, 151936, 1.0), (5, 151936, 0.7), (64, 151936, 1.3), (3, 1000, 1.0), (32, 151936, 0.9))
+    n = max(lib.orthrus_sample_workspace_bytes(r, V) for r, V, _ in shapes)
+    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    for rows, V, T in shapes:
+        z = llm_logits(rng, (rows, V))
+        u = uniforms(rng, rows)
+        out = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+        lib.orthrus_sample(f32_dev(z), T, f32_dev(u), out, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), sample_rows(z, T, u)), (rows, V, T)
+    cases = ((31, 4, 32, 151936, 0.8, 0.9), (32, 1, 32, 151936, 1.0, 0.95), (33, 4, 8, 3000, 1.2, 0.7))
+    n = max(lib.orthrus_accept_sampled_workspace_bytes(B, K, V) for _, B, K, V, _, _ in cases)
+    wa = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+    for seed, B, K, V, T, agree in cases:
+        zd, za, d, u_acc, u_res = _consensus_case(seed, B, K, V, T, agree)
+        outs = [torch.full(s, -7, dtype=torch.int32, device="cuda") for s in ((B, K), (B,), (B,), (B,))]
+        lib.orthrus_accept_sampled(f32_dev(zd), f32_dev(za), i32_dev(d), T, f32_dev(u_acc), f32_dev(u_res),
+                                   *outs, workspace=wa)
+        torch.cuda.synchronize()
+        ref = speculative_accept(zd, za, d, T, u_acc, u_res)
+        for got, want in zip(outs, ref):
+            assert np.array_equal(got.cpu().numpy(), want), (seed, B, K)
+    # and the consensus workspace then serves orthrus_sample too
+    z = llm_logits(rng, (64, 151936))
+    u = uniforms(rng, 64)
+    out = torch.full((64,), -7, dtype=torch.int32, device="cuda")
+    assert lib.orthrus_sample_workspace_bytes(64, 151936) <= wa.numel()
+    lib.orthrus_sample(f32_dev(z), 1.0, f32_dev(u), out, workspace=wa)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), sample_rows(z, 1.0, u))
 
 
 def test_sample_frequencies_on_a_uniform_grid(lib):
@@ -97,6 +135,7 @@ def run_accept(lib, zd, za, d, T, u_acc, u_res):
     (3, 8, 8, 3000, 1.5, 0.8),
     (4, 3, 1, 500, 1.0, 0.5),          # K = 1: every step emits one AR-distributed token
     (5, 2, 64, 2048, 0.5, 0.98),
+    (6, 1, 64, 151936, 0.9, 0.9),      # K = 64 at the 8B vocabulary: 149 chunks per row, 8 threads per row
 ])
 def test_accept_sampled_matches_oracle(lib, seed, B, K, V, T, agree):
     from oracle.sampling import speculative_accept
