@@ -1,16 +1,19 @@
-// e^x in fp64 for the non-positive arguments of the sampling kernels
-// (softmax weights exp((z - max) / T)).  Own implementation, table-driven:
-//   x = (64 k + j) ln2 / 64 + r, with 64 k + j the integer nearest 64 x / ln2,
-//   0 <= j < 64 and |r| <= ln2 / 128;
-//   e^x = 2^k * 2^(j/64) * e^r,  e^r = 1 + r + r^2/2 + r^3/6 + r^4/24 + r^5/120
-//   (the omitted terms are below 3.5e-17 relative).
-// The reduction is Cody-Waite: ln2 / 64 = kC1 + kC2 with kC1 rounded to 36
-// significant bits, so n * kC1 is exact for |n| < 2^17 (all x >= -750).
+// 2^(t/64) in fp64 for t <= 0: the sampling kernels' softmax weights
+// exp((z - max) / T) = 2^(t/64) with t = (z - max) * (64 / (T ln2)).  Own
+// implementation, table-driven:
+//   t = 64 k + j + f, with 64 k + j = n the integer nearest t, 0 <= j < 64
+//   and |f| <= 1/2 (f = t - n is exact);
+//   2^(t/64) = 2^k * 2^(j/64) * e^(f c),  c = ln2 / 64,
+//   e^(f c) - 1 = sum_{i=1..5} (f c)^i / i!   (the omitted terms are below
+//   3.5e-17 relative, as |f c| <= 0.0055).
 // kExp2Frac[j] is 2^(j/64) correctly rounded to fp64 (from a 60-digit decimal
-// evaluation).  Arguments below -750 give +0 (e^x < 2^-1075 rounds to zero
-// anyway); elsewhere the result is within 2 ulp of the exact value.  About 13
-// fp64 instructions and one table read (from LDS in the kernels), against
-// about 45 instructions for the general library exp.
+// evaluation), and the series coefficients c^i / i! likewise.  t below
+// -69300 (2^(t/64) < 2^-1082) gives +0.  Within 2 ulp of 2^(t/64) for the t
+// given; t itself carries the rounding of its own computation (relative
+// 2^-52 or so, i.e. an absolute error of about |x| 2^-52 in the exponent x
+// of e^x), as the argument of any fp64 exp would.  About 12 fp64
+// instructions and one table read (from LDS in the kernels), against about
+// 45 for the general library exp.
 #pragma once
 
 #if defined(__HIPCC__)
@@ -41,23 +44,22 @@ constexpr double kExp2Frac[64] = {
     0x1.d5818dcfba487p+0, 0x1.da9e603db3285p+0, 0x1.dfc97337b9b5fp+0, 0x1.e502ee78b3ff6p+0,
     0x1.ea4afa2a490dap+0, 0x1.efa1bee615a27p+0, 0x1.f50765b6e4540p+0, 0x1.fa7c1819e90d8p+0};
 
+// 64 / ln2: t = x * kExp2Scale turns e^x into 2^(t/64)
+constexpr double kExp2Scale = 0x1.71547652b82fep+6;
+
 // tab: kExp2Frac or a copy of it (the kernels keep one in LDS)
-ORTHRUS_HD inline double exp_nonpos(double x, const double* tab) {
-  const double k64OverLn2 = 0x1.71547652b82fep+6;
-  const double kC1 = 0x1.62e42fefa0000p-7;     // ln2 / 64 to 36 bits
-  const double kC2 = 0x1.cf79abc9e3b3ap-46;    // ln2 / 64 - kC1
-  x = x < -750.0 ? -750.0 : x;
-  const double t = std::rint(x * k64OverLn2);
-  double r = std::fma(-t, kC1, x);
-  r = std::fma(-t, kC2, r);
-  const int n = static_cast<int>(t);
-  const int j = n & 63;                         // n = 64 k + j, k = floor(n / 64)
-  const int k = n >> 6;
-  double p = std::fma(r, 0x1.1111111111111p-7, 0x1.5555555555555p-5);   // 1/120, 1/24
-  p = std::fma(p, r, 0x1.5555555555555p-3);                             // 1/6
-  p = std::fma(p, r, 0.5);
-  p = std::fma(p, r, 1.0);
-  p = p * r;                                                            // e^r - 1
+ORTHRUS_HD inline double exp2_64(double t, const double* tab) {
+  t = t < -69300.0 ? -69300.0 : t;
+  const double n = std::rint(t);
+  const double f = t - n;
+  const int ni = static_cast<int>(n);
+  const int j = ni & 63;                        // n = 64 k + j, k = floor(n / 64)
+  const int k = ni >> 6;
+  double p = std::fma(f, 0x1.5d87fe78a6731p-40, 0x1.3b2ab6fba4e77p-31);
+  p = std::fma(p, f, 0x1.c6b08d704a0c0p-23);
+  p = std::fma(p, f, 0x1.ebfbdff82c58fp-15);
+  p = std::fma(p, f, 0x1.62e42fefa39efp-7);
+  p = p * f;                                    // e^(f c) - 1
   return std::ldexp(std::fma(tab[j], p, tab[j]), k);
 }
 

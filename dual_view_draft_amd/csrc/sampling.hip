@@ -31,6 +31,7 @@
 // evaluation except within about 1e-15 (relative) of its threshold.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdint>
 
@@ -63,7 +64,7 @@ struct StatsArgs {
   float* cm;           // [rows][nchunks]
   double* cs;          // [rows][nchunks]
   int rows0, rows, V, chunk, nchunks;
-  double inv_t;
+  double tscale;
 };
 
 struct SampleArgs {
@@ -74,7 +75,7 @@ struct SampleArgs {
   double* cw;          // [rows][nchunks], used when the weights do not fit in LDS
   int32_t* out;        // [rows]
   int V, chunk, nchunks;
-  double inv_t;
+  double tscale;
 };
 
 struct DecideArgs {
@@ -90,7 +91,7 @@ struct DecideArgs {
   int32_t* next_anchor;
   SeqState* seq;       // [B]
   int B, K, V, nchunks;
-  double inv_t;
+  double tscale;
 };
 
 struct ResidualArgs {
@@ -104,7 +105,7 @@ struct ResidualArgs {
   int32_t* tokens;
   int32_t* next_anchor;
   int B, K, V, chunk, nchunks, rchunk, rchunks;
-  double inv_t;
+  double tscale;
 };
 
 // Every kernel keeps the 2^(j/64) table of its exponential in LDS; a
@@ -113,50 +114,108 @@ __device__ __forceinline__ void load_exp_table(double* tab) {
   if (threadIdx.x < 64) tab[threadIdx.x] = kExp2Frac[threadIdx.x];
 }
 
-// exp((z - m) / T) for z <= m (every caller passes a maximum as m)
-__device__ __forceinline__ double wexp(float z, float m, double inv_t, const double* tab) {
-  return exp_nonpos((double(z) - double(m)) * inv_t, tab);
+// exp((z - m) / T) = 2^(t/64) with t = (z - m) tscale, tscale = 64 / (T ln2),
+// for z <= m (every caller passes a maximum as m)
+__device__ __forceinline__ double wexp(float z, float m, double tscale, const double* tab) {
+  return exp2_64((double(z) - double(m)) * tscale, tab);
 }
 
-// Sum (or max) over a 256-thread workgroup in a fixed order: wavefront
-// butterflies, then the four wavefront results in order.
+// ---- wavefront and workgroup reductions in a fixed order -------------------
+// Within each row of 16 lanes, DPP row shifts (no LDS traffic) form an
+// inclusive scan (Hillis-Steele, shifts 1, 2, 4, 8); the four row results
+// are then combined in row order through lane reads.  Lanes whose shifted
+// source lies outside the row keep `fill`.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v, float fill) {
+  return __int_as_float(dpp_i32<CTRL>(__float_as_int(v), __float_as_int(fill)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v, double fill) {
+  const int lo = dpp_i32<CTRL>(__double2loint(v), __double2loint(fill));
+  const int hi = dpp_i32<CTRL>(__double2hiint(v), __double2hiint(fill));
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), lane),
+                          __builtin_amdgcn_readlane(__double2loint(v), lane));
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+
+// Sum over the wavefront, the same value in every lane.
+__device__ __forceinline__ double wave_sum(double v) {
+  v += dpp_f64<kRowShr1>(v, 0.0);
+  v += dpp_f64<kRowShr2>(v, 0.0);
+  v += dpp_f64<kRowShr4>(v, 0.0);
+  v += dpp_f64<kRowShr8>(v, 0.0);
+  return ((readlane_f64(v, 15) + readlane_f64(v, 31)) + readlane_f64(v, 47)) + readlane_f64(v, 63);
+}
+
+// Maximum over the wavefront, the same value in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<kRowShr1>(v, -INFINITY));
+  v = fmaxf(v, dpp_f32<kRowShr2>(v, -INFINITY));
+  v = fmaxf(v, dpp_f32<kRowShr4>(v, -INFINITY));
+  v = fmaxf(v, dpp_f32<kRowShr8>(v, -INFINITY));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = max(v, dpp_i32<kRowShr1>(v, INT_MIN));
+  v = max(v, dpp_i32<kRowShr2>(v, INT_MIN));
+  v = max(v, dpp_i32<kRowShr4>(v, INT_MIN));
+  v = max(v, dpp_i32<kRowShr8>(v, INT_MIN));
+  return max(max(__builtin_amdgcn_readlane(v, 15), __builtin_amdgcn_readlane(v, 31)),
+             max(__builtin_amdgcn_readlane(v, 47), __builtin_amdgcn_readlane(v, 63)));
+}
+
+// Sum (or max) over a 256-thread workgroup: the wavefront results, then the
+// four of them in order.  One barrier: a second call on the same `red`
+// needs a barrier between the two.
 __device__ double block_sum(double x, double* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  __syncthreads();
+  x = wave_sum(x);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
   return ((red[0] + red[1]) + red[2]) + red[3];
 }
 
 __device__ float block_max(float x, float* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  __syncthreads();
+  x = wave_max(x);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 // Inclusive and exclusive prefix sums of one value per thread over the
-// workgroup, in a fixed order (a wavefront scan, then the wavefront totals in
-// order), and the workgroup's maximum of one int per thread.  incl of thread
-// t is bitwise the excl of thread t+1, so "excl <= target < incl" holds for
-// at most one thread.
+// workgroup, in a fixed order (the row scans, the rows of a wavefront in
+// order, then the wavefront totals in order), and the workgroup's maximum of
+// one int per thread.  incl of thread t is bitwise the excl of thread t+1,
+// so "excl <= target < incl" holds for at most one thread.  One barrier: a
+// second call needs a barrier between the two.
 __device__ void block_scan(double x, int k, double* excl, double* incl, double* total, int* kmax) {
   __shared__ double wsum[kThreads / 64];
   __shared__ int wmax[kThreads / 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  double v = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(v, off);
-    if (lane >= off) v += y;
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) k = max(k, __shfl_xor(k, off));
-  double ve = __shfl_up(v, 1);
-  if (lane == 0) ve = 0.0;
+  double v = x;                                    // scan within the row of 16 lanes
+  v += dpp_f64<kRowShr1>(v, 0.0);
+  v += dpp_f64<kRowShr2>(v, 0.0);
+  v += dpp_f64<kRowShr4>(v, 0.0);
+  v += dpp_f64<kRowShr8>(v, 0.0);
+  const double o1 = readlane_f64(v, 15);           // row offsets: the rows before, in order
+  const double o2 = o1 + readlane_f64(v, 31);
+  const double o3 = o2 + readlane_f64(v, 47);
+  const int row = lane >> 4;
+  const double off = row == 0 ? 0.0 : row == 1 ? o1 : row == 2 ? o2 : o3;
+  v = off + v;                                     // lane 16r-1 ends as o_r exactly
+  const double ve = dpp_f64<kRowShr1>(v, off);     // the previous lane's, o_r at a row start
+  k = wave_max_i32(k);
   if (lane == 63) {
     wsum[w] = v;
     wmax[w] = k;
@@ -176,17 +235,16 @@ __device__ void block_scan(double x, int k, double* excl, double* incl, double* 
   *excl = pw + ve;
   *total = pre[kThreads / 64];
   *kmax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-  __syncthreads();
 }
 
 // Entries of a softmax row: weight exp((z - M) / T).
 struct SoftmaxEntry {
   const float* z;
   float M;
-  double inv_t;
+  double tscale;
   const double* tab;
   __device__ float load(int v) const { return z[v]; }
-  __device__ double weight(float zv) const { return wexp(zv, M, inv_t, tab); }
+  __device__ double weight(float zv) const { return wexp(zv, M, tscale, tab); }
 };
 
 // Entries of a residual row: weight max(0, p - q).
@@ -194,12 +252,12 @@ struct ResidualEntry {
   const float* za;
   const float* zd;
   float Ma, Md;
-  double Za, Zd, inv_t;
+  double Za, Zd, tscale;
   const double* tab;
   __device__ float2 load(int v) const { return float2{za[v], zd[v]}; }
   __device__ double weight(float2 e) const {
-    const double p = wexp(e.x, Ma, inv_t, tab) / Za;
-    const double q = wexp(e.y, Md, inv_t, tab) / Zd;
+    const double p = wexp(e.x, Ma, tscale, tab) / Za;
+    const double q = wexp(e.y, Md, tscale, tab) / Zd;
     return p > q ? p - q : 0.0;
   }
 };
@@ -215,10 +273,13 @@ struct ResidualEntry {
 // returns the token.
 template <int SHARE, class ChunkW, class Entry>
 __device__ int draw(ChunkW chunk_w, const Entry& entry, int nchunks, int chunk, int V, double u) {
-  __shared__ int pick_s;
+  __shared__ int pick_s, pick2_s;
   __shared__ double rem_s;
   const int tid = threadIdx.x;
-  if (tid == 0) pick_s = -1;                       // (ordered before any write by block_scan's barrier)
+  if (tid == 0) {                                  // (ordered before any write by block_scan's barrier)
+    pick_s = -1;
+    pick2_s = -1;
+  }
   // ---- level 1: which chunk -------------------------------------------------
   const int cpt = (nchunks + kThreads - 1) / kThreads;
   const int c0 = min(tid * cpt, nchunks), c1 = min(c0 + cpt, nchunks);
@@ -250,8 +311,6 @@ __device__ int draw(ChunkW chunk_w, const Entry& entry, int nchunks, int chunk, 
   int cstar = pick_s;
   double rem = rem_s;
   if (cstar < 0) { cstar = lastc_all < 0 ? 0 : lastc_all; rem = INFINITY; }   // target beyond the row
-  __syncthreads();                                 // everyone has read pick_s
-  if (tid == 0) pick_s = -1;
   // ---- level 2: which entry of chunk cstar -----------------------------------
   // A thread's share (at most SHARE entries) is loaded at once (addresses
   // clamped into the chunk, so that no load waits on a branch), its weights
@@ -302,10 +361,10 @@ __device__ int draw(ChunkW chunk_w, const Entry& entry, int nchunks, int chunk, 
         }
       }
     }
-    pick_s = found;
+    pick2_s = found;
   }
   __syncthreads();
-  const int tok = pick_s >= 0 ? pick_s : lastv_all;
+  const int tok = pick2_s >= 0 ? pick2_s : lastv_all;
   return tok < 0 ? v0 : tok;
 }
 
@@ -314,7 +373,7 @@ __device__ int draw(ChunkW chunk_w, const Entry& entry, int nchunks, int chunk, 
 // The second half of them is requested only once the first half has
 // arrived, and the first half's exponentials (relative to that half's
 // maximum) run while it is in flight; the lane's two partial sums and then
-// the wavefront's are rescaled to the larger maximum (fixed butterflies).
+// the wavefront's are rescaled to the larger maximum (fixed order).
 __global__ __launch_bounds__(kThreads) void sample_stats_kernel(StatsArgs a) {
   __shared__ double tab[64];
   constexpr int PER = kSampleChunk / 64, H = PER / 2;
@@ -340,28 +399,24 @@ __global__ __launch_bounds__(kThreads) void sample_stats_kernel(StatsArgs a) {
   // Entries past the chunk hold -inf and add exp(-inf) = +0 exactly (no
   // branch per entry); a half with no entries at all has m = -inf, and its
   // NaN sum is replaced by 0.
-  const double inv_t = a.inv_t;
+  const double tscale = a.tscale;
   float m1 = -INFINITY;
 #pragma unroll
   for (int j = 0; j < H; ++j) m1 = fmaxf(m1, x[j]);
   double s1 = 0.0;                                 // in increasing v, as the entries were read
 #pragma unroll
-  for (int j = 0; j < H; ++j) s1 += wexp(x[j], m1, inv_t, tab);
+  for (int j = 0; j < H; ++j) s1 += wexp(x[j], m1, tscale, tab);
   s1 = m1 == -INFINITY ? 0.0 : s1;
   float m2 = m1;
 #pragma unroll
   for (int j = H; j < PER; ++j) m2 = fmaxf(m2, x[j]);
   double s2 = 0.0;
 #pragma unroll
-  for (int j = H; j < PER; ++j) s2 += wexp(x[j], m2, inv_t, tab);
+  for (int j = H; j < PER; ++j) s2 += wexp(x[j], m2, tscale, tab);
   s2 = m2 == -INFINITY ? 0.0 : s2;
-  double sl = (m1 == m2 ? s1 : s1 * wexp(m1, m2, inv_t, tab)) + s2;   // the lane's sum relative to m2
-  float m = m2;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  double sw = m2 == m ? sl : sl * wexp(m2, m, inv_t, tab);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sw += __shfl_xor(sw, off);
+  double sl = (m1 == m2 ? s1 : s1 * wexp(m1, m2, tscale, tab)) + s2;   // the lane's sum relative to m2
+  const float m = wave_max(m2);
+  const double sw = wave_sum(m2 == m ? sl : sl * wexp(m2, m, tscale, tab));
   if (lane == 0) {
     a.cm[size_t(row) * a.nchunks + c] = m;
     a.cs[size_t(row) * a.nchunks + c] = sw;
@@ -391,18 +446,20 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a) {
   M = block_max(M, redf);                          // (its barriers also publish the table)
   const bool in_lds = a.nchunks <= kMaxChunksInLds;
   if (k0 < a.nchunks) {
-    const double w = cs0 * wexp(cm0, M, a.inv_t, tab);
+    const double w = cs0 * wexp(cm0, M, a.tscale, tab);
     if (in_lds) cw_s[k0] = w;
     else cw[k0] = w;
   }
   for (int k = k0 + kThreads; k < a.nchunks; k += kThreads) {
-    const double w = cs[k] * wexp(cm[k], M, a.inv_t, tab);
+    const double w = cs[k] * wexp(cm[k], M, a.tscale, tab);
     if (in_lds) cw_s[k] = w;
     else cw[k] = w;
   }
-  __syncthreads();
+  // Up to one chunk per thread, the draw's first level reads only the
+  // weight its own thread wrote; past that, shares span other threads' writes.
+  if (a.nchunks > kThreads) __syncthreads();
   const int tok = draw<kSampleChunk / kThreads>([&](int k) { return in_lds ? cw_s[k] : cw[k]; },
-                              SoftmaxEntry{a.z + size_t(row) * a.V, M, a.inv_t, tab}, a.nchunks, a.chunk, a.V, u);
+                              SoftmaxEntry{a.z + size_t(row) * a.V, M, a.tscale, tab}, a.nchunks, a.chunk, a.V, u);
   if (threadIdx.x == 0) a.out[row] = tok;
 }
 
@@ -467,7 +524,7 @@ __global__ __launch_bounds__(kDecideThreads) void sample_decide_kernel(DecideArg
     double zs = 0.0;
 #pragma unroll
     for (int q = 0; q < kReg; ++q)
-      if (gl + q * G < a.nchunks) zs += sv[q] * wexp(mv[q], m, a.inv_t, tab);   // uniform but for the last
+      if (gl + q * G < a.nchunks) zs += sv[q] * wexp(mv[q], m, a.tscale, tab);   // uniform but for the last
     for (int k0 = gl + kReg * G; k0 < a.nchunks; k0 += kReg * G) {
       float mb[kReg];
       double sb[kReg];
@@ -479,7 +536,7 @@ __global__ __launch_bounds__(kDecideThreads) void sample_decide_kernel(DecideArg
       }
 #pragma unroll
       for (int q = 0; q < kReg; ++q) {
-        const double w = sb[q] * wexp(mb[q], m, a.inv_t, tab);
+        const double w = sb[q] * wexp(mb[q], m, a.tscale, tab);
         zs += k0 + q * G < a.nchunks ? w : 0.0;
       }
     }
@@ -497,8 +554,8 @@ __global__ __launch_bounds__(kDecideThreads) void sample_decide_kernel(DecideArg
     na = rn_s[a.K + i];
     double p = 0.0, q = 0.0;                       // a token outside the vocabulary has p = q = 0
     if (in_vocab) {
-      p = wexp(zta, na.M, a.inv_t, tab) / na.Z;
-      q = wexp(ztd, nd.M, a.inv_t, tab) / nd.Z;
+      p = wexp(zta, na.M, a.tscale, tab) / na.Z;
+      q = wexp(ztd, nd.M, a.tscale, tab) / nd.Z;
     }
     reject = !(double(uacc) * q < p);
   }
@@ -527,7 +584,7 @@ __global__ __launch_bounds__(kThreads) void residual_stats_kernel(ResidualArgs a
   load_exp_table(tab);
   __syncthreads();
   const size_t row = size_t(b) * a.K + st.j;
-  const ResidualEntry r{a.za + row * a.V, a.zd + row * a.V, st.Ma, st.Md, st.Za, st.Zd, a.inv_t, tab};
+  const ResidualEntry r{a.za + row * a.V, a.zd + row * a.V, st.Ma, st.Md, st.Za, st.Zd, a.tscale, tab};
   const int v0 = c * a.rchunk, v1 = min(v0 + a.rchunk, a.V);
   double s = 0.0;
   for (int v = v0 + threadIdx.x; v < v1; v += kThreads) s += r.weight(r.load(v));
@@ -562,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void residual_draw_kernel(ResidualArgs a)
   const double u = double(u_s[st.j]);
   int tok;
   if (nonempty) {
-    const ResidualEntry r{a.za + row * a.V, a.zd + row * a.V, st.Ma, st.Md, st.Za, st.Zd, a.inv_t, tab};
+    const ResidualEntry r{a.za + row * a.V, a.zd + row * a.V, st.Ma, st.Md, st.Za, st.Zd, a.tscale, tab};
     tok = draw<kResidualChunk / kThreads>([&](int k) { return in_lds ? rs_s[k] : rs[k]; }, r, a.rchunks,
                                           a.rchunk, a.V, u);
   } else {
@@ -570,9 +627,9 @@ __global__ __launch_bounds__(kThreads) void residual_draw_kernel(ResidualArgs a)
     const float* cm = a.cm + srow * a.nchunks;
     const double* cs = a.cs + srow * a.nchunks;
     const float M = st.Ma;
-    const double inv_t = a.inv_t;
-    tok = draw<kSampleChunk / kThreads>([&](int k) { return cs[k] * wexp(cm[k], M, inv_t, tab); },
-                                           SoftmaxEntry{a.za + row * a.V, M, inv_t, tab}, a.nchunks, a.chunk, a.V,
+    const double tscale = a.tscale;
+    tok = draw<kSampleChunk / kThreads>([&](int k) { return cs[k] * wexp(cm[k], M, tscale, tab); },
+                                           SoftmaxEntry{a.za + row * a.V, M, tscale, tab}, a.nchunks, a.chunk, a.V,
                                            u);
   }
   if (threadIdx.x == 0) {
@@ -611,11 +668,11 @@ static_assert(kResidualChunk % (4 * kThreads) == 0 && kSampleChunk == 64 * 16 &&
 hipError_t launch_sample(const SamplePlan& p, const float* logits, float temperature, const float* u,
                          int32_t* out, void* ws, hipStream_t stream) {
   const Ws w = carve(p, ws);
-  const double inv_t = 1.0 / double(temperature);
+  const double tscale = kExp2Scale / double(temperature);   // 64 / (T ln2)
   hipError_t e = launch_stats(p, StatsArgs{logits, logits, w.cm, w.cs, p.rows, p.rows, p.V, p.chunk, p.nchunks,
-                                           inv_t}, stream);
+                                           tscale}, stream);
   if (e != hipSuccess) return e;
-  const SampleArgs d{logits, u, w.cm, w.cs, w.cw, out, p.V, p.chunk, p.nchunks, inv_t};
+  const SampleArgs d{logits, u, w.cm, w.cs, w.cw, out, p.V, p.chunk, p.nchunks, tscale};
   return launch_kernel(&sample_draw_kernel, dim3(p.rows), dim3(kThreads), stream, d);
 }
 
@@ -624,16 +681,16 @@ hipError_t launch_accept_sampled(const SamplePlan& p, const float* logits_d, con
                                  const float* u_res, int32_t* tokens, int32_t* n_acc, int32_t* n_emit,
                                  int32_t* next_anchor, void* ws, hipStream_t stream) {
   const Ws w = carve(p, ws);
-  const double inv_t = 1.0 / double(temperature);
+  const double tscale = kExp2Scale / double(temperature);   // 64 / (T ln2)
   hipError_t e = launch_stats(p, StatsArgs{logits_d, logits_a, w.cm, w.cs, B * K, p.rows, p.V, p.chunk,
-                                           p.nchunks, inv_t}, stream);
+                                           p.nchunks, tscale}, stream);
   if (e != hipSuccess) return e;
   const DecideArgs d{logits_d, logits_a, draft, u_acc, w.cm, w.cs, tokens, n_acc, n_emit, next_anchor, w.seq,
-                     B, K, p.V, p.nchunks, inv_t};
+                     B, K, p.V, p.nchunks, tscale};
   e = launch_kernel(&sample_decide_kernel, dim3(B), dim3(kDecideThreads), stream, d);
   if (e != hipSuccess) return e;
   const ResidualArgs r{logits_d, logits_a, u_res, w.cm, w.cs, w.seq, w.rs, tokens, next_anchor,
-                       B, K, p.V, p.chunk, p.nchunks, p.rchunk, p.rchunks, inv_t};
+                       B, K, p.V, p.chunk, p.nchunks, p.rchunk, p.rchunks, tscale};
   e = launch_kernel(&residual_stats_kernel, dim3(p.rchunks, B), dim3(kThreads), stream, r);
   if (e != hipSuccess) return e;
   return launch_kernel(&residual_draw_kernel, dim3(B), dim3(kThreads), stream, r);

@@ -112,35 +112,42 @@ int main() {
 
   for (int s : {0, -1, -2, -3, -4, -5, -99}) EXPECT(std::string(status_string(s)).rfind("ORTHRUS_", 0) == 0);
 
-  // the sampling kernels' exp for x <= 0: within 2 ulp of the C library's
-  // exp on a dense grid of [-760, 0] plus landmarks (0, the table and
-  // reduction boundaries, the underflow region), exactly 0 far below; and
-  // the table is 2^(j/64) to within half an ulp of the library's exp2
+  // the sampling kernels' 2^(t/64) for t <= 0: within 2 ulp of the C
+  // library's exp2 on a dense grid of [-69300, 0] plus landmarks (0, the
+  // table and rounding boundaries n + 1/2, the underflow region), exactly 0
+  // far below; the table is 2^(j/64) to within half an ulp of exp2; and
+  // e^x through t = x * 64/ln2 stays within 2^-51 (1 + |x|) (relative) of exp
   {
     for (int j = 0; j < 64; ++j) {
       const double want = std::exp2(j / 64.0);
       EXPECT(std::fabs(kExp2Frac[j] - want) <= 0.5 * (std::nextafter(want, 4.0) - want));
     }
     double worst = 0.0;
-    auto check = [&](double x) {
-      const double got = exp_nonpos(x, kExp2Frac), want = std::exp(x);
+    auto check = [&](double t) {
+      const double got = exp2_64(t, kExp2Frac), want = std::exp2(t / 64.0);
       if (want < 0x1p-1022) { EXPECT(std::fabs(got - want) <= 0x1p-1070); return; }
       const double ulp = std::nextafter(want, 1e300) - want;
       worst = std::max(worst, std::fabs(got - want) / ulp);
     };
-    for (int i = 0; i <= 4000000; ++i) check(-760.0 * i / 4000000.0);
-    for (int n = -2000; n <= 0; ++n) {           // around every reduction boundary (n + 1/2) ln2 / 64
-      const double b = (n + 0.5) * 0.6931471805599453 / 64;
-      check(b);
-      check(std::nextafter(b, 0.0));
-      check(std::nextafter(b, -1.0));
+    for (int i = 0; i <= 4000000; ++i) check(-69300.0 * i / 4000000.0);
+    for (int n = -70000; n <= 0; n += 7) {         // around the rounding boundaries n + 1/2
+      check(n + 0.5);
+      check(std::nextafter(n + 0.5, 0.0));
+      check(std::nextafter(n + 0.5, -1e9));
+      check(double(n));
     }
-    for (double x : {0.0, -0.0, -1e-300, -1e-17, -708.3, -708.4, -745.1, -745.2, -750.0})
-      check(x);
-    EXPECT(exp_nonpos(-1e30, kExp2Frac) == 0.0 && exp_nonpos(-800.0, kExp2Frac) == 0.0);
-    EXPECT(exp_nonpos(0.0, kExp2Frac) == 1.0);
+    for (double t : {0.0, -0.0, -1e-300, -1e-17, -65000.0, -65472.0, -68800.0, -69300.0})
+      check(t);
+    EXPECT(exp2_64(-1e30, kExp2Frac) == 0.0 && exp2_64(-80000.0, kExp2Frac) == 0.0);
+    EXPECT(exp2_64(0.0, kExp2Frac) == 1.0);
     EXPECT(worst <= 2.0);
-    std::printf("exp_nonpos: worst %.2f ulp\n", worst);
+    double worst_x = 0.0;
+    for (int i = 1; i <= 200000; ++i) {
+      const double x = -700.0 * i / 200000.0, want = std::exp(x);
+      worst_x = std::max(worst_x, std::fabs(exp2_64(x * kExp2Scale, kExp2Frac) - want) / (want * (1.0 - x)));
+    }
+    EXPECT(worst_x <= 0x1p-51);
+    std::printf("exp2_64: worst %.2f ulp; e^x via t: %.3g (1 + |x|) relative\n", worst, worst_x);
   }
   std::printf("%s (%d failures)\n", failures ? "FAIL" : "OK", failures);
   return failures ? 1 : 0;
