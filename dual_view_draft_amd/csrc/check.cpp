@@ -278,16 +278,20 @@ bool plan_sample(int stat_rows, int B, int V, SamplePlan* p) {
   p->rows = stat_rows;
   p->B = B;
   p->V = V;
-  p->chunk = kSampleChunk;
-  p->nchunks = int(ceil_div(V, kSampleChunk));
+  const int64_t rows1 = stat_rows > 0 ? stat_rows : 1;
+  const int64_t waves = rows1 * round_up(ceil_div(V, kSampleChunk), kSampleGroup);
+  p->chunk = waves <= kSampleResidentWaves ? kSampleChunk : kSampleChunkLarge;
+  p->nchunks = int(ceil_div(V, p->chunk));
+  p->ngroups = int(ceil_div(p->nchunks, kSampleGroup));
   p->rchunk = kResidualChunk;
   p->rchunks = B > 0 ? int(ceil_div(V, kResidualChunk)) : 0;
-  const int64_t rows1 = stat_rows > 0 ? stat_rows : 1;
-  const int64_t cells = rows1 * p->nchunks;
+  const int64_t cells = rows1 * p->nchunks, gcells = rows1 * p->ngroups;
   p->cm_off = 0;
   p->cs_off = p->cm_off + size_t(round_up(cells * 4, 256));
   p->cw_off = p->cs_off + size_t(round_up(cells * 8, 256));
-  p->seq_off = p->cw_off + size_t(round_up(cells * 8, 256));
+  p->gm_off = p->cw_off + size_t(round_up(cells * 8, 256));
+  p->gs_off = p->gm_off + size_t(round_up(gcells * 4, 256));
+  p->seq_off = p->gs_off + size_t(round_up(gcells * 8, 256));
   p->rs_off = p->seq_off + size_t(round_up(int64_t(B > 0 ? B : 1) * kSampleSeqBytes, 256));
   p->ws_bytes = p->rs_off + size_t(round_up(int64_t(B > 0 ? B : 1) * (p->rchunks > 0 ? p->rchunks : 1) * 8, 256));
   return true;
@@ -302,7 +306,7 @@ int check_sample(const float* logits, int rows, int V, float temperature, const 
     return fail(err, ORTHRUS_ERR_INVALID_ARG, "temperature must be finite and > 0");
   plan_sample(rows, 0, V, plan);
   if (int64_t(rows) * plan->nchunks > kMaxSampleCells)
-    return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "rows * ceil(vocab / 1024) must be <= 2^30");
+    return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "rows * (statistics chunks per row) must be <= 2^30");
   if (rows == 0) return ORTHRUS_OK;
   if (!logits || !u || !out) return fail(err, ORTHRUS_ERR_INVALID_ARG, "null logits/u/out");
   if (!ws || !aligned16(ws)) return fail(err, ORTHRUS_ERR_INVALID_ARG, "workspace null or misaligned");
@@ -325,7 +329,7 @@ int check_accept_sampled(const float* logits_d, const float* logits_a, const int
     return fail(err, ORTHRUS_ERR_INVALID_ARG, "temperature must be finite and > 0");
   plan_sample(2 * B * K, B, V, plan);
   if (int64_t(2 * B * K) * plan->nchunks > kMaxSampleCells)
-    return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "2 * batch * block_k * ceil(vocab / 1024) must be <= 2^30");
+    return fail(err, ORTHRUS_ERR_UNSUPPORTED_SHAPE, "2 * batch * block_k * (statistics chunks per row) must be <= 2^30");
   if (B == 0) return ORTHRUS_OK;
   if (!logits_d || !logits_a || !draft || !u_acc || !u_res || !tokens || !n_acc || !n_emit || !next_anchor)
     return fail(err, ORTHRUS_ERR_INVALID_ARG, "null pointer argument");

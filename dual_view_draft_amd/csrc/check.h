@@ -104,14 +104,21 @@ int check_commit(const orthrus_kv* kv, int layers, int64_t pool_layer_stride, co
 // per-sequence acceptance state and the residual chunk sums.
 constexpr int kSampleSeqBytes = 32;
 constexpr int kResidualChunk = 1024;   // entries per residual chunk
-constexpr int kSampleChunk = 1024;     // entries per statistics chunk (one wavefront, 16 per lane)
+// Statistics chunks: one wavefront each, 16 entries per lane (1024), or 32
+// per lane (2048) when the 1024-entry chunks would need more wavefronts than
+// the GPU holds at once; four consecutive chunks of a row form a group.
+constexpr int kSampleChunk = 1024;
+constexpr int kSampleChunkLarge = 2048;
+constexpr int kSampleGroup = 4;
+constexpr int64_t kSampleResidentWaves = 7168;   // 256 CUs x 4 SIMDs x 7 wavefronts
 constexpr int64_t kMaxSampleCells = int64_t(1) << 30;   // statistics rows x chunks per call at most
 
 struct SamplePlan {
   int rows = 0;          // rows with chunk statistics
   int B = 0, V = 0, chunk = 0, nchunks = 0;
+  int ngroups = 0;               // groups of kSampleGroup chunks per row
   int rchunk = 0, rchunks = 0;   // residual chunks (consensus only)
-  size_t cm_off = 0, cs_off = 0, cw_off = 0, seq_off = 0, rs_off = 0, ws_bytes = 0;
+  size_t cm_off = 0, cs_off = 0, cw_off = 0, gm_off = 0, gs_off = 0, seq_off = 0, rs_off = 0, ws_bytes = 0;
 };
 
 // stat_rows: rows of orthrus_sample, or 2*B*K for the consensus (B sequences).

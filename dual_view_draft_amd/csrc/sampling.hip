@@ -63,7 +63,9 @@ struct StatsArgs {
   const float* z1;     // rows [rows0, rows)
   float* cm;           // [rows][nchunks]
   double* cs;          // [rows][nchunks]
-  int rows0, rows, V, chunk, nchunks;
+  float* gm;           // [rows][ngroups] the same over groups of kSampleGroup chunks (null: not wanted)
+  double* gs;
+  int rows0, rows, V, nchunks, ngroups;
   double tscale;
 };
 
@@ -83,14 +85,14 @@ struct DecideArgs {
   const float* za;     // [B*K][V] AR view
   const int32_t* draft;
   const float* u_acc;  // [B][K]
-  const float* cm;     // statistics rows: draft rows, then AR rows
-  const double* cs;
+  const float* gm;     // group statistics rows: draft rows, then AR rows
+  const double* gs;
   int32_t* tokens;     // [B][K]
   int32_t* n_acc;
   int32_t* n_emit;
   int32_t* next_anchor;
   SeqState* seq;       // [B]
-  int B, K, V, nchunks;
+  int B, K, V, ngroups;
   double tscale;
 };
 
@@ -369,63 +371,107 @@ __device__ int draw(ChunkW chunk_w, const Entry& entry, int nchunks, int chunk, 
 }
 
 // Chunk statistics of every row: m_c and s_c = sum exp((z - m_c) / T), one
-// wavefront per (row, chunk), lane l taking entries v0 + l + 64 j (j < 16).
-// The second half of them is requested only once the first half has
-// arrived, and the first half's exponentials (relative to that half's
-// maximum) run while it is in flight; the lane's two partial sums and then
-// the wavefront's are rescaled to the larger maximum (fixed order).
+// wavefront per (row, chunk), lane l taking entries v0 + l + 64 j
+// (j < PER, chunks of 64 PER entries).  The second half of them is
+// requested only once the first half has arrived, and the first half's
+// exponentials (relative to that half's maximum) run while it is in flight;
+// the lane's two partial sums and then the wavefront's are rescaled to the
+// larger maximum (fixed order).  A workgroup holds kSampleGroup consecutive
+// chunks of one row and also writes their combined statistics (in chunk
+// order).
+template <int PER>
 __global__ __launch_bounds__(kThreads) void sample_stats_kernel(StatsArgs a) {
   __shared__ double tab[64];
-  constexpr int PER = kSampleChunk / 64, H = PER / 2;
+  __shared__ float wm[kSampleGroup];
+  __shared__ double ws[kSampleGroup];
+  static_assert(kThreads == 64 * kSampleGroup, "a wavefront per chunk of the group");
+  constexpr int H = PER / 2;
+  static_assert(H % 4 == 0, "blocks of 4 exponentials");
   const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);   // row * nchunks + chunk
-  const bool live = unit < a.rows * a.nchunks;     // (at most 2^30 units)
-  const int row = live ? unit / a.nchunks : 0;
-  const int c = live ? unit - row * a.nchunks : 0;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // (uniform: scalar registers below)
+  const int row = blockIdx.x / a.ngroups;
+  const int g = blockIdx.x - row * a.ngroups;
+  const int c = g * kSampleGroup + w;
+  const bool live = c < a.nchunks;
   const float* z = row < a.rows0 ? a.z0 + size_t(row) * a.V : a.z1 + size_t(row - a.rows0) * a.V;
-  const int v0 = c * kSampleChunk, v1 = live ? min(v0 + kSampleChunk, a.V) : v0;
-  const int vt = v0 + lane;
+  const int v0 = c * (64 * PER), n = live ? min(64 * PER, a.V - v0) : 0;   // entries in the chunk
+  // The chunk through a buffer descriptor of n entries: one address register
+  // for all loads, and loads past the chunk's end return 0 (then -inf below).
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(z) + (live ? v0 : 0), 0, n * 4, 0x00020000);
   float x[PER];
 #pragma unroll
-  for (int j = 0; j < H; ++j) x[j] = vt + j * 64 < v1 ? z[vt + j * 64] : -INFINITY;
+  for (int j = 0; j < H; ++j)
+    x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, lane * 4, j * 256, 0));
   load_exp_table(tab);
   __syncthreads();
-  if (!live) return;                               // uniform per wavefront, after the only barrier
-  // the second half's addresses wait on the first half's data
-  int vb = vt;
-  asm volatile("" : "+v"(vb) : "v"(x[H - 1]));
+  // the second half's offsets wait on the first half's data
+  int lb = lane * 4;
+  asm volatile("" : "+v"(lb) : "v"(x[H - 1]));
 #pragma unroll
-  for (int j = H; j < PER; ++j) x[j] = vt + j * 64 < v1 ? z[vb + j * 64] : -INFINITY;
+  for (int j = H; j < PER; ++j)
+    x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, lb, j * 256, 0));
+#pragma unroll
+  for (int j = 0; j < H; ++j) x[j] = lane + j * 64 < n ? x[j] : -INFINITY;
   // Entries past the chunk hold -inf and add exp(-inf) = +0 exactly (no
   // branch per entry); a half with no entries at all has m = -inf, and its
-  // NaN sum is replaced by 0.
+  // NaN sum is replaced by 0 (a wavefront past the last chunk ends with
+  // m = -inf, s = 0).
   const double tscale = a.tscale;
   float m1 = -INFINITY;
 #pragma unroll
   for (int j = 0; j < H; ++j) m1 = fmaxf(m1, x[j]);
+  // (the exponentials in blocks of 4, kept apart by scheduling barriers so
+  // that the compiler does not interleave them all and raise the register
+  // count, which would cut the wavefronts resident per SIMD)
   double s1 = 0.0;                                 // in increasing v, as the entries were read
 #pragma unroll
-  for (int j = 0; j < H; ++j) s1 += wexp(x[j], m1, tscale, tab);
+  for (int jb = 0; jb < H; jb += 4) {
+#pragma unroll
+    for (int j = jb; j < jb + 4; ++j) s1 += wexp(x[j], m1, tscale, tab);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   s1 = m1 == -INFINITY ? 0.0 : s1;
+#pragma unroll
+  for (int j = H; j < PER; ++j) x[j] = lane + j * 64 < n ? x[j] : -INFINITY;
   float m2 = m1;
 #pragma unroll
   for (int j = H; j < PER; ++j) m2 = fmaxf(m2, x[j]);
   double s2 = 0.0;
 #pragma unroll
-  for (int j = H; j < PER; ++j) s2 += wexp(x[j], m2, tscale, tab);
+  for (int jb = H; jb < PER; jb += 4) {
+#pragma unroll
+    for (int j = jb; j < jb + 4; ++j) s2 += wexp(x[j], m2, tscale, tab);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   s2 = m2 == -INFINITY ? 0.0 : s2;
-  double sl = (m1 == m2 ? s1 : s1 * wexp(m1, m2, tscale, tab)) + s2;   // the lane's sum relative to m2
+  const double sl = (m1 == m2 ? s1 : s1 * wexp(m1, m2, tscale, tab)) + s2;   // the lane's sum relative to m2
   const float m = wave_max(m2);
   const double sw = wave_sum(m2 == m ? sl : sl * wexp(m2, m, tscale, tab));
-  if (lane == 0) {
+  if (lane == 0 && live) {
     a.cm[size_t(row) * a.nchunks + c] = m;
     a.cs[size_t(row) * a.nchunks + c] = sw;
+  }
+  if (a.gm == nullptr) return;                     // (uniform) no group statistics wanted
+  if (lane == 0) {
+    wm[w] = m;
+    ws[w] = sw;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {                          // chunk 0 of the group is always live
+    const float gmax = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+    double gsum = 0.0;
+#pragma unroll
+    for (int q = 0; q < kSampleGroup; ++q) gsum += wm[q] == gmax ? ws[q] : ws[q] * wexp(wm[q], gmax, tscale, tab);
+    a.gm[size_t(row) * a.ngroups + g] = gmax;
+    a.gs[size_t(row) * a.ngroups + g] = gsum;
   }
 }
 
 // One workgroup per row: the row maximum M, every chunk's weight
 // s_c exp((m_c - M) / T) (into LDS, or global memory past kMaxChunksInLds
 // chunks), then out[row] = draw of softmax(z[row] / T) with u[row].
+template <int SHARE>
 __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a) {
   __shared__ float redf[4];
   __shared__ double tab[64];
@@ -458,14 +504,15 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a) {
   // Up to one chunk per thread, the draw's first level reads only the
   // weight its own thread wrote; past that, shares span other threads' writes.
   if (a.nchunks > kThreads) __syncthreads();
-  const int tok = draw<kSampleChunk / kThreads>([&](int k) { return in_lds ? cw_s[k] : cw[k]; },
+  const int tok = draw<SHARE>([&](int k) { return in_lds ? cw_s[k] : cw[k]; },
                               SoftmaxEntry{a.z + size_t(row) * a.V, M, a.tscale, tab}, a.nchunks, a.chunk, a.V, u);
   if (threadIdx.x == 0) a.out[row] = tok;
 }
 
 // One workgroup per sequence: the maximum and normaliser of each of its 2K
-// statistics rows (a group of G threads per row, chunks strided over the
-// group, then a butterfly within the group), then wavefront 0, lane i = block
+// statistics rows from their group statistics (a team of G threads per row,
+// groups strided over the team, then a butterfly within it), then
+// wavefront 0, lane i = block
 // row i, runs the acceptance test of every row and finds the first
 // rejection.
 constexpr int kDecideThreads = 1024;
@@ -483,8 +530,8 @@ __global__ __launch_bounds__(kDecideThreads) void sample_decide_kernel(DecideArg
   const int r = threadIdx.x / G, gl = threadIdx.x % G;
   const bool has_row = r < R;                      // whole groups: G divides 64
   const size_t srow = (r < a.K ? size_t(b) * a.K + r : size_t(BK) + size_t(b) * a.K + (r - a.K));
-  const float* cm = a.cm + (has_row ? srow : 0) * a.nchunks;
-  const double* cs = a.cs + (has_row ? srow : 0) * a.nchunks;
+  const float* cm = a.gm + (has_row ? srow : 0) * a.ngroups;
+  const double* cs = a.gs + (has_row ? srow : 0) * a.ngroups;
   // every independent load first: the rows' first batch of statistics, and
   // for wavefront 0 (lane i = block row i) the drafted token, its uniform
   // and its logits
@@ -498,7 +545,7 @@ __global__ __launch_bounds__(kDecideThreads) void sample_decide_kernel(DecideArg
 #pragma unroll
   for (int q = 0; q < kReg; ++q) {
     const int k = gl + q * G;
-    const bool ok = has_row && k < a.nchunks;
+    const bool ok = has_row && k < a.ngroups;
     mv[q] = ok ? cm[k] : -INFINITY;
     sv[q] = ok ? cs[k] : 0.0;
   }
@@ -511,10 +558,10 @@ __global__ __launch_bounds__(kDecideThreads) void sample_decide_kernel(DecideArg
     float m = -INFINITY;
 #pragma unroll
     for (int q = 0; q < kReg; ++q) m = fmaxf(m, mv[q]);
-    for (int k0 = gl + kReg * G; k0 < a.nchunks; k0 += kReg * G) {   // further batches (large vocabularies)
+    for (int k0 = gl + kReg * G; k0 < a.ngroups; k0 += kReg * G) {   // further batches (large vocabularies)
       float mb[kReg];
 #pragma unroll
-      for (int q = 0; q < kReg; ++q) mb[q] = k0 + q * G < a.nchunks ? cm[k0 + q * G] : -INFINITY;
+      for (int q = 0; q < kReg; ++q) mb[q] = k0 + q * G < a.ngroups ? cm[k0 + q * G] : -INFINITY;
 #pragma unroll
       for (int q = 0; q < kReg; ++q) m = fmaxf(m, mb[q]);
     }
@@ -524,20 +571,20 @@ __global__ __launch_bounds__(kDecideThreads) void sample_decide_kernel(DecideArg
     double zs = 0.0;
 #pragma unroll
     for (int q = 0; q < kReg; ++q)
-      if (gl + q * G < a.nchunks) zs += sv[q] * wexp(mv[q], m, a.tscale, tab);   // uniform but for the last
-    for (int k0 = gl + kReg * G; k0 < a.nchunks; k0 += kReg * G) {
+      if (gl + q * G < a.ngroups) zs += sv[q] * wexp(mv[q], m, a.tscale, tab);   // uniform but for the last
+    for (int k0 = gl + kReg * G; k0 < a.ngroups; k0 += kReg * G) {
       float mb[kReg];
       double sb[kReg];
 #pragma unroll
       for (int q = 0; q < kReg; ++q) {
-        const bool ok = k0 + q * G < a.nchunks;
+        const bool ok = k0 + q * G < a.ngroups;
         mb[q] = ok ? cm[k0 + q * G] : -INFINITY;
         sb[q] = ok ? cs[k0 + q * G] : 0.0;
       }
 #pragma unroll
       for (int q = 0; q < kReg; ++q) {
         const double w = sb[q] * wexp(mb[q], m, a.tscale, tab);
-        zs += k0 + q * G < a.nchunks ? w : 0.0;
+        zs += k0 + q * G < a.ngroups ? w : 0.0;
       }
     }
 #pragma unroll
@@ -628,7 +675,7 @@ __global__ __launch_bounds__(kThreads) void residual_draw_kernel(ResidualArgs a)
     const double* cs = a.cs + srow * a.nchunks;
     const float M = st.Ma;
     const double tscale = a.tscale;
-    tok = draw<kSampleChunk / kThreads>([&](int k) { return cs[k] * wexp(cm[k], M, tscale, tab); },
+    tok = draw<kSampleChunkLarge / kThreads>([&](int k) { return cs[k] * wexp(cm[k], M, tscale, tab); },
                                            SoftmaxEntry{a.za + row * a.V, M, tscale, tab}, a.nchunks, a.chunk, a.V,
                                            u);
   }
@@ -642,6 +689,8 @@ struct Ws {
   float* cm;
   double* cs;
   double* cw;
+  float* gm;
+  double* gs;
   SeqState* seq;
   double* rs;
 };
@@ -649,31 +698,35 @@ struct Ws {
 Ws carve(const SamplePlan& p, void* ws) {
   char* base = static_cast<char*>(ws);
   return Ws{reinterpret_cast<float*>(base + p.cm_off), reinterpret_cast<double*>(base + p.cs_off),
-            reinterpret_cast<double*>(base + p.cw_off), reinterpret_cast<SeqState*>(base + p.seq_off),
+            reinterpret_cast<double*>(base + p.cw_off), reinterpret_cast<float*>(base + p.gm_off),
+            reinterpret_cast<double*>(base + p.gs_off), reinterpret_cast<SeqState*>(base + p.seq_off),
             reinterpret_cast<double*>(base + p.rs_off)};
 }
 
 hipError_t launch_stats(const SamplePlan& p, const StatsArgs& s, hipStream_t stream) {
-  const int64_t units = int64_t(p.rows) * p.nchunks;
-  const dim3 grid(unsigned((units + kThreads / 64 - 1) / (kThreads / 64)));
-  return launch_kernel(&sample_stats_kernel, grid, dim3(kThreads), stream, s);
+  const dim3 grid(unsigned(int64_t(p.rows) * p.ngroups));
+  if (p.chunk == kSampleChunk)
+    return launch_kernel(&sample_stats_kernel<kSampleChunk / 64>, grid, dim3(kThreads), stream, s);
+  return launch_kernel(&sample_stats_kernel<kSampleChunkLarge / 64>, grid, dim3(kThreads), stream, s);
 }
 
 }  // namespace
 
 static_assert(sizeof(SeqState) == kSampleSeqBytes, "per-sequence state size");
-static_assert(kResidualChunk % (4 * kThreads) == 0 && kSampleChunk == 64 * 16 && kSampleChunk % (4 * kThreads) == 0,
-              "chunk shares");
+static_assert(kResidualChunk % (4 * kThreads) == 0 && kSampleChunk % (4 * kThreads) == 0 &&
+              kSampleChunkLarge % (4 * kThreads) == 0 && kSampleChunk == 64 * 16, "chunk shares");
 
 hipError_t launch_sample(const SamplePlan& p, const float* logits, float temperature, const float* u,
                          int32_t* out, void* ws, hipStream_t stream) {
   const Ws w = carve(p, ws);
   const double tscale = kExp2Scale / double(temperature);   // 64 / (T ln2)
-  hipError_t e = launch_stats(p, StatsArgs{logits, logits, w.cm, w.cs, p.rows, p.rows, p.V, p.chunk, p.nchunks,
-                                           tscale}, stream);
+  hipError_t e = launch_stats(p, StatsArgs{logits, logits, w.cm, w.cs, nullptr, nullptr, p.rows, p.rows, p.V,
+                                           p.nchunks, p.ngroups, tscale}, stream);
   if (e != hipSuccess) return e;
   const SampleArgs d{logits, u, w.cm, w.cs, w.cw, out, p.V, p.chunk, p.nchunks, tscale};
-  return launch_kernel(&sample_draw_kernel, dim3(p.rows), dim3(kThreads), stream, d);
+  if (p.chunk == kSampleChunk)
+    return launch_kernel(&sample_draw_kernel<kSampleChunk / kThreads>, dim3(p.rows), dim3(kThreads), stream, d);
+  return launch_kernel(&sample_draw_kernel<kSampleChunkLarge / kThreads>, dim3(p.rows), dim3(kThreads), stream, d);
 }
 
 hipError_t launch_accept_sampled(const SamplePlan& p, const float* logits_d, const float* logits_a,
@@ -682,11 +735,11 @@ hipError_t launch_accept_sampled(const SamplePlan& p, const float* logits_d, con
                                  int32_t* next_anchor, void* ws, hipStream_t stream) {
   const Ws w = carve(p, ws);
   const double tscale = kExp2Scale / double(temperature);   // 64 / (T ln2)
-  hipError_t e = launch_stats(p, StatsArgs{logits_d, logits_a, w.cm, w.cs, B * K, p.rows, p.V, p.chunk,
-                                           p.nchunks, tscale}, stream);
+  hipError_t e = launch_stats(p, StatsArgs{logits_d, logits_a, w.cm, w.cs, w.gm, w.gs, B * K, p.rows, p.V,
+                                           p.nchunks, p.ngroups, tscale}, stream);
   if (e != hipSuccess) return e;
-  const DecideArgs d{logits_d, logits_a, draft, u_acc, w.cm, w.cs, tokens, n_acc, n_emit, next_anchor, w.seq,
-                     B, K, p.V, p.nchunks, tscale};
+  const DecideArgs d{logits_d, logits_a, draft, u_acc, w.gm, w.gs, tokens, n_acc, n_emit, next_anchor, w.seq,
+                     B, K, p.V, p.ngroups, tscale};
   e = launch_kernel(&sample_decide_kernel, dim3(B), dim3(kDecideThreads), stream, d);
   if (e != hipSuccess) return e;
   const ResidualArgs r{logits_d, logits_a, u_res, w.cm, w.cs, w.seq, w.rs, tokens, next_anchor,

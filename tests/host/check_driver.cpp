@@ -89,14 +89,19 @@ int main() {
   EXPECT(plan_lmhead(300, 1024, 20011, &lp, nullptr) && lp.gemm == 1);
   EXPECT(!plan_lmhead(32, 4000, 151936, &lp, nullptr));   // hidden not a multiple of 64
 
-  // sampling statistics: chunks of 1024 entries; 4.2 M words make 4102
-  // chunks (more than the 1024 whose weights a draw keeps in LDS)
+  // sampling statistics: chunks of 1024 entries while their wavefronts fit on
+  // the GPU at once (152 per row of 151936: up to 47 rows), else 2048; groups
+  // of 4 chunks; 4.2 M words make 4102 chunks (more than the 1024 whose
+  // weights a draw keeps in LDS)
   SamplePlan sp;
-  EXPECT(plan_sample(32, 0, 151936, &sp) && sp.chunk == 1024 && sp.nchunks == 149);
-  EXPECT(plan_sample(2 * 16 * 32, 16, 151936, &sp) && sp.nchunks == 149 && sp.rchunks == 149);
-  EXPECT(sp.cs_off >= size_t(1024) * 149 * 4 && sp.rs_off + size_t(16) * sp.rchunks * 8 <= sp.ws_bytes);
-  EXPECT(plan_sample(1, 0, 4200000, &sp) && sp.nchunks == 4102);
-  EXPECT(plan_sample(7, 0, 1000, &sp) && sp.nchunks == 1);
+  EXPECT(plan_sample(32, 0, 151936, &sp) && sp.chunk == 1024 && sp.nchunks == 149 && sp.ngroups == 38);
+  EXPECT(plan_sample(47, 0, 151936, &sp) && sp.chunk == 1024);
+  EXPECT(plan_sample(48, 0, 151936, &sp) && sp.chunk == 2048 && sp.nchunks == 75 && sp.ngroups == 19);
+  EXPECT(plan_sample(2 * 16 * 32, 16, 151936, &sp) && sp.nchunks == 75 && sp.rchunks == 149);
+  EXPECT(sp.cs_off >= size_t(1024) * 75 * 4 && sp.gs_off >= sp.gm_off + size_t(1024) * 19 * 4);
+  EXPECT(sp.rs_off + size_t(16) * sp.rchunks * 8 <= sp.ws_bytes);
+  EXPECT(plan_sample(1, 0, 4200000, &sp) && sp.nchunks == 4102 && sp.ngroups == 1026);
+  EXPECT(plan_sample(7, 0, 1000, &sp) && sp.nchunks == 1 && sp.ngroups == 1);
   // at most 2^30 (row, chunk) cells per call
   EXPECT(check_sample(reinterpret_cast<const float*>(P), 65535, 1 << 26, 1.0f, reinterpret_cast<const float*>(P), I, P, size_t(1) << 50, &sp, &err) == ORTHRUS_ERR_UNSUPPORTED_SHAPE);
   EXPECT(check_sample(reinterpret_cast<const float*>(P), 1024, 1 << 20, 1.0f, reinterpret_cast<const float*>(P), I, P, size_t(1) << 50, &sp, &err) == ORTHRUS_OK);

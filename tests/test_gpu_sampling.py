@@ -43,8 +43,10 @@ def uniforms(rng, shape):
 
 # 1 x 4.2 M words: more than 1024 statistics chunks per row, so the draw reads
 # the chunk weights from global memory instead of LDS
+# 48 x 151936: 2048-entry statistics chunks (1024-entry ones would need more
+# wavefronts than the GPU holds at once)
 @pytest.mark.parametrize("rows,V,T", [(32, 151936, 1.0), (32, 151936, 0.6), (7, 1000, 2.5), (1, 1, 1.0),
-                                      (65, 5000, 0.3), (3, 20000, 1.0), (1, 4200000, 0.8)])
+                                      (65, 5000, 0.3), (3, 20000, 1.0), (1, 4200000, 0.8), (48, 151936, 0.8)])
 def test_sample_matches_oracle(lib, rows, V, T):
     from oracle.sampling import sample_rows
     rng = np.random.default_rng(rows * 7 + V)
