@@ -23,6 +23,7 @@
 #include <cstdint>
 
 #include "check.h"
+#include "dpp.h"
 #include "keys.h"
 #include "launch.h"
 
@@ -53,15 +54,8 @@ struct AcceptArgs {
   int B, K, nchunks, lpr;
 };
 
-__device__ __forceinline__ unsigned long long wave_max(unsigned long long k) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(k), off);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(k >> 32), off);
-    k = umax64(k, (static_cast<unsigned long long>(hi) << 32) | lo);
-  }
-  return k;
-}
+// (the maximum of 64-bit keys does not depend on the order of reduction)
+__device__ __forceinline__ unsigned long long wave_max(unsigned long long k) { return wave_max_u64(k); }
 
 __global__ __launch_bounds__(256) void argmax_partial_kernel(PartialArgs a) {
   constexpr int UNR = 4;                         // float4 loads in flight per thread
