@@ -15,4 +15,5 @@ from .binding import (ORTHRUS_KV_BF16, ORTHRUS_KV_FP8_E4M3, ORTHRUS_MAX_BLOCK,  
                       orthrus_lmhead_accept, orthrus_lmhead_argmax, orthrus_lmhead_workspace_bytes,
                       orthrus_quantize_kv, orthrus_status_string, orthrus_sample,
                       orthrus_sample_workspace_bytes, orthrus_accept_sampled,
-                      orthrus_accept_sampled_workspace_bytes)
+                      orthrus_accept_sampled_workspace_bytes, orthrus_device_errors, device_errors,
+                      DEVERR_SEQ_LEN, DEVERR_PAGE_ID, DEVERR_N_EMIT)

@@ -47,6 +47,7 @@ EXPORTS = {
     "orthrus_abi_version": (ctypes.c_int, []),
     "orthrus_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "orthrus_last_error": (ctypes.c_char_p, []),
+    "orthrus_device_errors": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
     "orthrus_attn_split_tokens": (ctypes.c_int, [ctypes.c_int] * 3),
     "orthrus_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 7),
     "orthrus_attn_draft": (ctypes.c_int, [ctypes.POINTER(orthrus_kv)] + [ctypes.c_void_p] * 4 +
@@ -420,3 +421,24 @@ def orthrus_accept_sampled(logits_d: torch.Tensor, logits_a: torch.Tensor, draft
                                                _ptr(n_acc), _ptr(n_emit), _ptr(next_anchor), _ptr(workspace),
                                                workspace.numel(), _stream(stream))
     _check(rc, "orthrus_accept_sampled")
+
+
+DEVERR_SEQ_LEN, DEVERR_PAGE_ID, DEVERR_N_EMIT = 1, 2, 4
+
+
+def orthrus_device_errors(out: torch.Tensor, *, clear: bool = True, stream=None) -> torch.Tensor:
+    """Copy the GPU's device error word (ORTHRUS_DEVERR_* bits) into `out`
+    (int32 or uint32-sized, one element, on the device), in stream order, and
+    reset it if `clear`."""
+    if out.numel() != 1 or out.element_size() != 4:
+        raise ValueError("out must hold one 32-bit element")
+    rc = load_library().orthrus_device_errors(_ptr(out), 1 if clear else 0, _stream(stream))
+    _check(rc, "orthrus_device_errors")
+    return out
+
+
+def device_errors(clear: bool = True) -> int:
+    """The current device's error word (synchronises the current stream)."""
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    orthrus_device_errors(out, clear=clear, stream=torch.cuda.current_stream())
+    return int(out.item())

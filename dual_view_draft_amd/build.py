@@ -21,7 +21,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "liborthrus.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn.hip", "consensus.hip", "lmhead.hip", "quant.hip", "sampling.hip", "commit.hip", "abi.cpp", "check.cpp"]
+SOURCES = ["attn.hip", "consensus.hip", "lmhead.hip", "quant.hip", "sampling.hip", "commit.hip", "deverr.hip",
+           "abi.cpp", "check.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-mcode-object-version=5", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

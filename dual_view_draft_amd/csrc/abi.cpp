@@ -3,6 +3,7 @@
 // exception escapes; failures return a status and set a thread-local message.
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
 #include <string>
 
 #include "check.h"
@@ -50,6 +51,16 @@ int orthrus_abi_version(void) { return ORTHRUS_ABI_VERSION; }
 const char* orthrus_status_string(int status) { return orthrus::status_string(status); }
 
 const char* orthrus_last_error(void) { return g_last_error.c_str(); }
+
+int orthrus_device_errors(uint32_t* flags, int clear, void* stream) {
+  try {
+    if (!flags || (reinterpret_cast<uintptr_t>(flags) & 3u))
+      return fail(ORTHRUS_ERR_INVALID_ARG, "flags must be a non-null, 4-byte aligned device pointer");
+    return hip_status(orthrus::launch_device_errors(flags, clear, as_stream(stream)));
+  } catch (...) {
+    return fail(ORTHRUS_ERR_HIP, "internal error");
+  }
+}
 
 int orthrus_attn_split_tokens(int batch, int num_kv_heads, int max_ctx) {
   return orthrus::attn_split_tokens(batch, num_kv_heads, max_ctx);

@@ -93,6 +93,7 @@ struct AttnArgs {
   const void* v_blk;
   uint16_t* part_o;  // [B][Hkv][nchunks][nsplit][rpc][D] bf16: O / l of the split
   float* part_ml;    // [B][Hkv][nchunks][nsplit][rpc][2]: m (log2 units), l
+  unsigned int* err; // the device error word (ORTHRUS_DEVERR_* bits)
   int B, K, Hq, Hkv, G, num_pages, maxp, max_ctx, split, nsplit, rows, nchunks, rpc;
   float scale_log2;
 };
@@ -268,6 +269,16 @@ __global__ __launch_bounds__(512, 1) void attn_split_kernel(AttnArgs a) {
   if (start >= N) return;                        // uniform across the workgroup
   const int end = min(start + a.split, N);
   const int ntiles = (end - start + kTile - 1) / kTile;   // <= kMaxSplitTiles
+  {
+    // Device-side preconditions: the length, and this wavefront's page of
+    // every tile of the split whose rows hold cached positions (lane i: tile
+    // i, rows start + 64 i + 8 wave ...).  A violation is clamped below and
+    // flagged in the error word (no cost when all hold but this check).
+    const bool bad_page = lane < ntiles && start + kTile * lane + 8 * wave < L &&
+                          static_cast<unsigned>(page_ids) >= static_cast<unsigned>(a.num_pages);
+    const unsigned bad = (L_raw != L ? ORTHRUS_DEVERR_SEQ_LEN : 0u) | (__ballot(bad_page) ? ORTHRUS_DEVERR_PAGE_ID : 0u);
+    if (bad && lane == 0) atomicOr(a.err, bad);
+  }
 
   // ---- where this wavefront's share of each tile comes from ---------------
   // Wavefront w fetches tile rows 8w .. 8w+7 (half of page w/2) of K and V.
@@ -775,6 +786,10 @@ hipError_t launch_attention(const AttnPlan& p, const orthrus_kv& kv, const void*
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_o_bytes);
   a.B = p.B; a.K = p.K; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G;
   a.num_pages = kv.num_pages; a.maxp = kv.max_pages_per_seq; a.max_ctx = p.max_ctx;
+  {
+    hipError_t e = device_error_word(&a.err);
+    if (e != hipSuccess) return e;
+  }
   a.split = p.split; a.nsplit = p.nsplit; a.rows = p.rows; a.nchunks = p.nchunks;
   a.rpc = p.rows_per_chunk;
   a.scale_log2 = float(double(scale) * 1.4426950408889634);

@@ -32,6 +32,7 @@ struct CommitArgs {
   const int32_t* n_emit;
   int32_t* seq_lens_out;
   int64_t pool_stride, blk_stride;   // bytes per layer
+  unsigned int* err;                 // the device error word (ORTHRUS_DEVERR_* bits)
   int B, K, Hkv, RB, num_pages, maxp;   // RB: bytes per head row
 };
 
@@ -41,16 +42,25 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
   const int layer = blockIdx.z;
   // A length beyond what the block table can address is clamped first, so
   // L + r stays far below 2^31.
-  const int L = int(min(int64_t(max(a.seq_lens[b], 0)), int64_t(a.maxp) * ORTHRUS_PAGE_SIZE));
-  int e = a.n_emit[b];
-  e = e < 0 ? 0 : (e > a.K ? a.K : e);
-  if (r == 0 && layer == 0 && threadIdx.x == 0) a.seq_lens_out[b] = L + e;
+  // Violated device-side preconditions are clamped and flagged in the error
+  // word (by one thread per sequence, or per row and layer 0).
+  const int L_raw = a.seq_lens[b];
+  const int L = int(min(int64_t(max(L_raw, 0)), int64_t(a.maxp) * ORTHRUS_PAGE_SIZE));
+  const int e_raw = a.n_emit[b];
+  const int e = e_raw < 0 ? 0 : (e_raw > a.K ? a.K : e_raw);
+  if (r == 0 && layer == 0 && threadIdx.x == 0) {
+    a.seq_lens_out[b] = L + e;
+    const unsigned bad = (L_raw != L ? ORTHRUS_DEVERR_SEQ_LEN : 0u) | (e_raw != e ? ORTHRUS_DEVERR_N_EMIT : 0u);
+    if (bad) atomicOr(a.err, bad);
+  }
   if (r >= e) return;
   const int p = L + r;
   const int pi = p >> 4;
-  if (pi >= a.maxp) return;
-  const int page = a.block_table[size_t(b) * a.maxp + pi];
-  if (static_cast<unsigned>(page) >= static_cast<unsigned>(a.num_pages)) return;
+  const int page = pi < a.maxp ? a.block_table[size_t(b) * a.maxp + pi] : -1;
+  if (static_cast<unsigned>(page) >= static_cast<unsigned>(a.num_pages)) {
+    if (layer == 0 && threadIdx.x == 0) atomicOr(a.err, ORTHRUS_DEVERR_PAGE_ID);
+    return;
+  }
   const int slot = p & 15;
   const int G16 = a.RB / 16;               // granules per head row
   const int per_tensor = a.Hkv * G16;
@@ -86,6 +96,8 @@ hipError_t launch_commit(const orthrus_kv& kv, int layers, int64_t pool_layer_st
   a.blk_stride = blk_layer_stride * es;
   a.B = B; a.K = K; a.Hkv = kv.num_kv_heads; a.RB = kv.head_dim * es;
   a.num_pages = kv.num_pages; a.maxp = kv.max_pages_per_seq;
+  hipError_t e = device_error_word(&a.err);
+  if (e != hipSuccess) return e;
   return launch_kernel(&commit_kernel, dim3(K, B, layers), dim3(256), stream, a);
 }
 

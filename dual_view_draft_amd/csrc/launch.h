@@ -26,6 +26,11 @@ hipError_t launch_attention(const AttnPlan& plan, const orthrus_kv& kv, const vo
 // (kStaticScratchBytes bytes), looked up once per device.
 hipError_t static_attn_scratch(void** ptr);
 
+// Device address of the current device's error word (ORTHRUS_DEVERR_* bits),
+// looked up once per device; and the call that copies (and clears) it.
+hipError_t device_error_word(unsigned int** ptr);
+hipError_t launch_device_errors(uint32_t* out, int clear, hipStream_t stream);
+
 hipError_t launch_argmax(const ArgmaxPlan& plan, const float* logits, int32_t* out, void* ws,
                          hipStream_t stream);
 

@@ -36,6 +36,7 @@
 #include <cstdint>
 
 #include "check.h"
+#include "dpp.h"
 #include "fexp.h"
 #include "launch.h"
 
@@ -122,61 +123,9 @@ __device__ __forceinline__ double wexp(float z, float m, double tscale, const do
   return exp2_64((double(z) - double(m)) * tscale, tab);
 }
 
-// ---- wavefront and workgroup reductions in a fixed order -------------------
-// Within each row of 16 lanes, DPP row shifts (no LDS traffic) form an
-// inclusive scan (Hillis-Steele, shifts 1, 2, 4, 8); the four row results
-// are then combined in row order through lane reads.  Lanes whose shifted
-// source lies outside the row keep `fill`.
-template <int CTRL>
-__device__ __forceinline__ int dpp_i32(int v, int fill) {
-  return __builtin_amdgcn_update_dpp(fill, v, CTRL, 0xf, 0xf, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v, float fill) {
-  return __int_as_float(dpp_i32<CTRL>(__float_as_int(v), __float_as_int(fill)));
-}
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v, double fill) {
-  const int lo = dpp_i32<CTRL>(__double2loint(v), __double2loint(fill));
-  const int hi = dpp_i32<CTRL>(__double2hiint(v), __double2hiint(fill));
-  return __hiloint2double(hi, lo);
-}
-__device__ __forceinline__ double readlane_f64(double v, int lane) {
-  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), lane),
-                          __builtin_amdgcn_readlane(__double2loint(v), lane));
-}
-constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
-
-// Sum over the wavefront, the same value in every lane.
-__device__ __forceinline__ double wave_sum(double v) {
-  v += dpp_f64<kRowShr1>(v, 0.0);
-  v += dpp_f64<kRowShr2>(v, 0.0);
-  v += dpp_f64<kRowShr4>(v, 0.0);
-  v += dpp_f64<kRowShr8>(v, 0.0);
-  return ((readlane_f64(v, 15) + readlane_f64(v, 31)) + readlane_f64(v, 47)) + readlane_f64(v, 63);
-}
-
-// Maximum over the wavefront, the same value in every lane.
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f32<kRowShr1>(v, -INFINITY));
-  v = fmaxf(v, dpp_f32<kRowShr2>(v, -INFINITY));
-  v = fmaxf(v, dpp_f32<kRowShr4>(v, -INFINITY));
-  v = fmaxf(v, dpp_f32<kRowShr8>(v, -INFINITY));
-  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
-  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
-  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
-}
-
-__device__ __forceinline__ int wave_max_i32(int v) {
-  v = max(v, dpp_i32<kRowShr1>(v, INT_MIN));
-  v = max(v, dpp_i32<kRowShr2>(v, INT_MIN));
-  v = max(v, dpp_i32<kRowShr4>(v, INT_MIN));
-  v = max(v, dpp_i32<kRowShr8>(v, INT_MIN));
-  return max(max(__builtin_amdgcn_readlane(v, 15), __builtin_amdgcn_readlane(v, 31)),
-             max(__builtin_amdgcn_readlane(v, 47), __builtin_amdgcn_readlane(v, 63)));
-}
+// ---- wavefront and workgroup reductions in a fixed order (dpp.h) ----------
+__device__ __forceinline__ double wave_sum(double v) { return wave_sum_f64(v); }
+__device__ __forceinline__ float wave_max(float v) { return wave_max_f32(v); }
 
 // Sum (or max) over a 256-thread workgroup: the wavefront results, then the
 // four of them in order.  One barrier: a second call on the same `red`
@@ -372,10 +321,8 @@ __device__ int draw(ChunkW chunk_w, const Entry& entry, int nchunks, int chunk, 
 
 // Chunk statistics of every row: m_c and s_c = sum exp((z - m_c) / T), one
 // wavefront per (row, chunk), lane l taking entries v0 + l + 64 j
-// (j < PER, chunks of 64 PER entries).  The second half of them is
-// requested only once the first half has arrived, and the first half's
-// exponentials (relative to that half's maximum) run while it is in flight;
-// the lane's two partial sums and then the wavefront's are rescaled to the
+// (j < PER, chunks of 64 PER entries), loaded in two stages (see below);
+// the lane's and then the wavefront's sums are rescaled to the
 // larger maximum (fixed order).  A workgroup holds kSampleGroup consecutive
 // chunks of one row and also writes their combined statistics (in chunk
 // order).
@@ -385,8 +332,11 @@ __global__ __launch_bounds__(kThreads) void sample_stats_kernel(StatsArgs a) {
   __shared__ float wm[kSampleGroup];
   __shared__ double ws[kSampleGroup];
   static_assert(kThreads == 64 * kSampleGroup, "a wavefront per chunk of the group");
-  constexpr int H = PER / 2;
-  static_assert(H % 4 == 0, "blocks of 4 exponentials");
+  // Two stages of loads: four stages of 8 at PER = 32 measured 1 % faster at
+  // 64 rows and 3 % slower at 512 and 1024 rows.
+  constexpr int kStage = PER / 2;                  // entries per lane per stage of loads
+  constexpr int S = PER / kStage;
+  static_assert(PER % kStage == 0 && kStage % 4 == 0, "stages of whole blocks of 4");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // (uniform: scalar registers below)
   const int row = blockIdx.x / a.ngroups;
@@ -401,51 +351,49 @@ __global__ __launch_bounds__(kThreads) void sample_stats_kernel(StatsArgs a) {
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(z) + (live ? v0 : 0), 0, n * 4, 0x00020000);
   float x[PER];
 #pragma unroll
-  for (int j = 0; j < H; ++j)
+  for (int j = 0; j < kStage; ++j)
     x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, lane * 4, j * 256, 0));
   load_exp_table(tab);
   __syncthreads();
-  // the second half's offsets wait on the first half's data
-  int lb = lane * 4;
-  asm volatile("" : "+v"(lb) : "v"(x[H - 1]));
-#pragma unroll
-  for (int j = H; j < PER; ++j)
-    x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, lb, j * 256, 0));
-#pragma unroll
-  for (int j = 0; j < H; ++j) x[j] = lane + j * 64 < n ? x[j] : -INFINITY;
-  // Entries past the chunk hold -inf and add exp(-inf) = +0 exactly (no
-  // branch per entry); a half with no entries at all has m = -inf, and its
-  // NaN sum is replaced by 0 (a wavefront past the last chunk ends with
-  // m = -inf, s = 0).
+  // Stage st's loads are issued once stage st-1 has arrived (their offsets
+  // wait on its data), and stage st-1's exponentials run while stage st is in
+  // flight.  Each stage's sum is relative to the running maximum; the running
+  // sum is rescaled when the maximum grows.  Entries past the chunk hold -inf
+  // and add exp(-inf) = +0 exactly (no branch per entry); while the maximum
+  // is still -inf (no entry yet) the NaN sums are replaced by 0, so a
+  // wavefront past the last chunk ends with m = -inf, s = 0.  (The
+  // exponentials go in blocks of 4, kept apart by scheduling barriers so that
+  // the compiler does not interleave them all and raise the register count,
+  // which would cut the wavefronts resident per SIMD.)
   const double tscale = a.tscale;
-  float m1 = -INFINITY;
+  float m2 = -INFINITY;                            // the lane's running maximum
+  double sl = 0.0;                                 // and its sum, in increasing v
 #pragma unroll
-  for (int j = 0; j < H; ++j) m1 = fmaxf(m1, x[j]);
-  // (the exponentials in blocks of 4, kept apart by scheduling barriers so
-  // that the compiler does not interleave them all and raise the register
-  // count, which would cut the wavefronts resident per SIMD)
-  double s1 = 0.0;                                 // in increasing v, as the entries were read
+  for (int st = 0; st < S; ++st) {
+    if (st + 1 < S) {
+      int lb = lane * 4;
+      asm volatile("" : "+v"(lb) : "v"(x[kStage * st + kStage - 1]));
 #pragma unroll
-  for (int jb = 0; jb < H; jb += 4) {
+      for (int j = kStage * (st + 1); j < kStage * (st + 2); ++j)
+        x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, lb, j * 256, 0));
+    }
 #pragma unroll
-    for (int j = jb; j < jb + 4; ++j) s1 += wexp(x[j], m1, tscale, tab);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int j = kStage * st; j < kStage * (st + 1); ++j) x[j] = lane + j * 64 < n ? x[j] : -INFINITY;
+    float ms = m2;
+#pragma unroll
+    for (int j = kStage * st; j < kStage * (st + 1); ++j) ms = fmaxf(ms, x[j]);
+    double ss = 0.0;
+#pragma unroll
+    for (int jb = kStage * st; jb < kStage * (st + 1); jb += 4) {
+#pragma unroll
+      for (int j = jb; j < jb + 4; ++j) ss += wexp(x[j], ms, tscale, tab);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    ss = ms == -INFINITY ? 0.0 : ss;
+    if (st == 0) sl = ss;                          // (the same as below with sl = 0, m2 = -inf)
+    else sl = (m2 == ms ? sl : sl * wexp(m2, ms, tscale, tab)) + ss;
+    m2 = ms;
   }
-  s1 = m1 == -INFINITY ? 0.0 : s1;
-#pragma unroll
-  for (int j = H; j < PER; ++j) x[j] = lane + j * 64 < n ? x[j] : -INFINITY;
-  float m2 = m1;
-#pragma unroll
-  for (int j = H; j < PER; ++j) m2 = fmaxf(m2, x[j]);
-  double s2 = 0.0;
-#pragma unroll
-  for (int jb = H; jb < PER; jb += 4) {
-#pragma unroll
-    for (int j = jb; j < jb + 4; ++j) s2 += wexp(x[j], m2, tscale, tab);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  s2 = m2 == -INFINITY ? 0.0 : s2;
-  const double sl = (m1 == m2 ? s1 : s1 * wexp(m1, m2, tscale, tab)) + s2;   // the lane's sum relative to m2
   const float m = wave_max(m2);
   const double sw = wave_sum(m2 == m ? sl : sl * wexp(m2, m, tscale, tab));
   if (lane == 0 && live) {

@@ -45,7 +45,8 @@
  *  - Device-side contents (page ids, sequence lengths, emitted counts) are
  *    preconditions the host cannot see.  Kernels clamp them so that no access
  *    leaves the buffers described here, but results are unspecified when they
- *    are violated.
+ *    are violated; each violation met also sets a bit of the GPU's device
+ *    error word (orthrus_device_errors).
  */
 #ifndef ORTHRUS_H
 #define ORTHRUS_H
@@ -125,6 +126,27 @@ ORTHRUS_API const char* orthrus_status_string(int status);
 
 /* Thread-local detail of the most recent failed call on this thread ("" if none). */
 ORTHRUS_API const char* orthrus_last_error(void);
+
+/*
+ * Device error word: one 32-bit word per GPU, zero when the library is first
+ * used on it, into which kernels OR these bits when they meet a violated
+ * device-side precondition (and clamp the value so that every access stays
+ * in bounds):
+ *  ORTHRUS_DEVERR_SEQ_LEN : a sequence length below 0, above max_ctx
+ *                           (attention) or beyond the block table (commit);
+ *  ORTHRUS_DEVERR_PAGE_ID : a page id outside [0, num_pages) where a cached
+ *                           position (attention) or a committed row (commit)
+ *                           needs it, or a committed row past the block table;
+ *  ORTHRUS_DEVERR_N_EMIT  : an emitted count outside [0, block_k] (commit).
+ * orthrus_device_errors enqueues, on `stream`, a copy of the current device's
+ * word into flags (device memory, one uint32) and, if clear != 0, resets the
+ * word to zero.  It sees what kernels earlier on the same stream set; kernels
+ * on other streams of the GPU may set bits at any time.  Allocates nothing.
+ */
+#define ORTHRUS_DEVERR_SEQ_LEN 1u
+#define ORTHRUS_DEVERR_PAGE_ID 2u
+#define ORTHRUS_DEVERR_N_EMIT 4u
+ORTHRUS_API int orthrus_device_errors(uint32_t* flags, int clear, void* stream);
 
 /*
  * Context split size in tokens chosen when split_tokens == 0 is passed to the

@@ -129,6 +129,12 @@ def test_host_checks_under_sanitizers(tmp_path):
     assert "OK (0 failures)" in r.stdout
 
 
+def test_device_errors_argument_checks(lib):
+    lib.orthrus_device_errors.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert lib.orthrus_device_errors(None, 1, None) == -1          # null flags pointer
+    assert lib.orthrus_device_errors(ctypes.c_void_p(0x10002), 0, None) == -1   # misaligned
+
+
 def test_lmhead_workspace_and_argument_checks(lib):
     P = ctypes.c_void_p(0x10000)
     n = lib.orthrus_lmhead_workspace_bytes(32, 4096, 151936)
