@@ -628,12 +628,13 @@ __device__ __forceinline__ float pair_max(float x, int off) {
 // (permlane swaps for lane distances 16 and 32).  Batches after the first
 // rescale the running sums when the maximum grows.  Splits a row cannot see
 // contribute exact zeros, so the result does not depend on how many splits
-// the call had.
-template <int D>
+// the call had.  U is 2 when the call has at most 2 SG splits (batched
+// decoding, whose many rows would otherwise issue 4 times the loads they
+// use), else 8; a row's splits meet in the same lanes and order either way.
+template <int D, int U>
 __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
   constexpr int TPR = D / 8;      // lanes per row slice
   constexpr int SG = 64 / TPR;    // split groups per wavefront
-  constexpr int U = 8;            // splits per lane group per batch
   constexpr int BATCH = U * SG;   // splits per batch
   const int lane = threadIdx.x & 63;
   // Workgroup -> (sequence b, KV head g) = id mod (B * Hkv), and 4 of that
@@ -809,8 +810,11 @@ hipError_t launch_attention(const AttnPlan& p, const orthrus_kv& kv, const void*
   c.B = p.B; c.K = p.K; c.Hq = p.Hq; c.G = p.G; c.max_ctx = p.max_ctx;
   c.split = p.split; c.nsplit = p.nsplit; c.nchunks = p.nchunks; c.rpc = p.rows_per_chunk;
   dim3 grid(unsigned((int64_t(p.K) * p.G + 3) / 4 * p.B * p.Hkv));
-  return p.D == 128 ? launch_kernel(&attn_combine_kernel<128>, grid, dim3(256), stream, c)
-                    : launch_kernel(&attn_combine_kernel<64>, grid, dim3(256), stream, c);
+  if (p.D == 128)
+    return p.nsplit <= 2 * 4 ? launch_kernel(&attn_combine_kernel<128, 2>, grid, dim3(256), stream, c)
+                             : launch_kernel(&attn_combine_kernel<128, 8>, grid, dim3(256), stream, c);
+  return p.nsplit <= 2 * 8 ? launch_kernel(&attn_combine_kernel<64, 2>, grid, dim3(256), stream, c)
+                           : launch_kernel(&attn_combine_kernel<64, 8>, grid, dim3(256), stream, c);
 }
 
 }  // namespace orthrus
