@@ -13,16 +13,19 @@
 // draw with a caller-supplied uniform: the smallest v whose cumulative weight
 // exceeds u times the total.
 //
-// Work layout.  Rows are cut into chunks of 1024 vocabulary entries; a
-// statistics pass (one wavefront per chunk, 16 entries per lane, no
-// barriers) writes, per (row, chunk), the chunk's maximum logit m_c (fp32)
-// and s_c = sum exp((z - m_c) / T) (fp64).  The next kernel forms a row's
-// maximum M, the chunk weights s_c exp((m_c - M) / T) and their sum Z in a
-// fixed order, and then draws (orthrus_sample) or runs the acceptance test
-// of a sequence's rows (consensus).  A draw (one 256-thread workgroup) finds
-// its chunk from the chunk weights and then its entry inside that chunk
-// (4 per thread), each time from a fixed-order prefix sum over contiguous
-// per-thread shares.  The residual of a rejected row has its own chunk sums.
+// Work layout.  Rows are cut into chunks of 1024 vocabulary entries (2048
+// when the 1024-entry chunks would need more wavefronts than the GPU holds
+// at once); a statistics pass (one wavefront per chunk, 16 or 32 entries per
+// lane, wavefront reductions only) writes, per (row, chunk), the chunk's
+// maximum logit m_c (fp32) and s_c = sum exp((z - m_c) / T) (fp64), and for
+// the consensus the same over groups of four chunks.  The next kernel forms
+// a row's maximum M, the chunk weights s_c exp((m_c - M) / T) and their sum Z
+// in a fixed order, and then draws (orthrus_sample) or runs the acceptance
+// test of a sequence's rows (consensus).  A draw (one 256-thread workgroup)
+// finds its chunk from the chunk weights and then its entry inside that
+// chunk (4 or 8 per thread), each time from a fixed-order prefix sum over
+// contiguous per-thread shares.  The residual of a rejected row has its own
+// chunk sums.
 // (Handing the chunk results to the row's last workgroup within one launch
 // was measured slower: a device-scope fence per workgroup, or device-scope
 // atomics for the hand-over, cost more than the second launch.)
@@ -43,7 +46,7 @@
 namespace orthrus {
 namespace {
 
-constexpr int kThreads = 256;          // every sampling kernel
+constexpr int kThreads = 256;          // every sampling kernel but the acceptance test
 constexpr int kMaxChunksInLds = 1024;  // chunk weights kept in LDS for a draw up to this many chunks
 
 struct RowNorm {       // a row's maximum and normaliser
