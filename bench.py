@@ -462,12 +462,24 @@ def main():
                      "mfma_tflops": round(attn_flops / (op_ms[dom8] * 1e-3) / 1e12, 1)},
     }
     logit_bytes = B * K * V * 4
+    samp_gbps = logit_bytes / (op_ms["draft_sample_t1"] * 1e-3) / 1e9
     res["sampling_t1"] = {
         "op_ms": {o: round(op_ms[o], 4) for o in ("draft_sample_t1", "accept_sampled_t1")},
-        "logits_gbps": {"draft_sample_t1": round(logit_bytes / (op_ms["draft_sample_t1"] * 1e-3) / 1e9, 1),
+        "logits_gbps": {"draft_sample_t1": round(samp_gbps, 1),
                         "accept_sampled_t1": round(2 * logit_bytes / (op_ms["accept_sampled_t1"] * 1e-3) / 1e9, 1)},
-        "note": "fp32 logits read once per statistics pass; fp64 exponentials",
+        "roofline": {"kernel": "draft_sample_t1: sample_stats_kernel + sample_draw_kernel (one ABI call)",
+                     "bound": "hbm", "achieved": round(samp_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(samp_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": logit_bytes},
+        "note": "fp32 logits read once per statistics pass (the draw rereads one chunk per row); "
+                "fp64 exponentials",
     }
+    # the consensus ops of the timed step, each one pass over one view's fp32 logits
+    res["consensus_roofline"] = {
+        o: {"bound": "hbm", "achieved": round(logit_bytes / (op_ms[o] * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(logit_bytes / (op_ms[o] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes_per_launch": logit_bytes}
+        for o in ("draft_argmax", "accept")}
     if args.workload == "qwen3_8b_40k" and not args.no_extra_workloads:
         res["qwen3_8b_4k"] = workload_object(args, torch, dv, synth, "qwen3_8b_4k")
         res["qwen3_8b_ragged16"] = workload_object(args, torch, dv, synth, "qwen3_8b_ragged16")

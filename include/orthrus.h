@@ -343,7 +343,10 @@ ORTHRUS_API size_t orthrus_sample_workspace_bytes(int rows, int vocab);
  *  logits : fp32 [rows][vocab], finite
  *  u      : fp32 [rows], each in [0, 1)
  *  out    : int32 [rows] (written)
- * 0 <= rows <= 65535 (0 = no-op); 1 <= vocab <= 2^30; temperature finite and > 0.
+ * 0 <= rows <= 65535 (0 = no-op); 1 <= vocab <= 2^30; rows * ceil(vocab / 1024)
+ * <= 2^30 (ORTHRUS_ERR_UNSUPPORTED_SHAPE beyond); temperature finite and > 0.
+ * The workspace holds per-call results only; its contents need no
+ * initialisation and are not read across calls.
  */
 ORTHRUS_API int orthrus_sample(const float* logits, int rows, int vocab, float temperature, const float* u,
                    int32_t* out, void* workspace, size_t workspace_bytes, void* stream);
@@ -367,8 +370,9 @@ ORTHRUS_API size_t orthrus_accept_sampled_workspace_bytes(int batch, int block_k
  *                       [0, n_emit), -1 after
  *  n_acc, n_emit, next_anchor : int32 [batch] (written), as in orthrus_accept
  * 1 <= block_k <= 64; 2 * batch * block_k <= 65535; 1 <= vocab <= 2^30;
- * temperature finite, > 0.  A drafted token outside [0, vocab) counts as
- * probability 0 in both views (always rejected).
+ * 2 * batch * block_k * ceil(vocab / 1024) <= 2^30; temperature finite, > 0.
+ * A drafted token outside [0, vocab) counts as probability 0 in both views
+ * (always rejected).  The workspace needs no initialisation.
  */
 ORTHRUS_API int orthrus_accept_sampled(const float* logits_d, const float* logits_a, const int32_t* draft,
                            int batch, int block_k, int vocab, float temperature, const float* u_acc,

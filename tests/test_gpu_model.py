@@ -138,6 +138,8 @@ def test_orthrus_matches_greedy_at_40k_context(setup, kv):
     if kv == "e4m3":
         s = torch.full((cfg.layers, cfg.Hkv), 1.0 / 32, dtype=torch.float32, device="cuda")
         scales = (s, s)
+    import dual_view_draft_amd as dv
+    dv.device_errors(clear=True)
     cache = ModelCache(cfg, LONG_L + LONG_N + 3 * K + 128, "cuda", seed=4, kv_scales=scales)
     first = 1234
     cache.fill_random(LONG_L, seed=9)
@@ -152,3 +154,4 @@ def test_orthrus_matches_greedy_at_40k_context(setup, kv):
     cache.fill_random(LONG_L, seed=9)
     toks, emits, _ = model.decode_orthrus(cache, first, 12, K)
     assert toks == ref[:12]
+    assert dv.device_errors(clear=True) == 0     # every length, page id and count the loops passed held
