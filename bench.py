@@ -407,6 +407,10 @@ def main():
         "tokens_per_step": {
             "realised": int(sum(min(int(a) + 1, K) for a in cons.n_acc)),
             "expected": round(B * sum(0.85 ** k for k in range(K)), 2),
+            # the same expectation for other per-token rejection rates p (the
+            # step's time does not depend on it; tokens/s = tokens/step x steps/s)
+            "expected_by_p": {str(pr): round(B * sum((1 - pr) ** k for k in range(K)), 2)
+                              for pr in (0.08, 0.15, 0.3)},
         },
         "settle": {"warmup_steps": args.warmup, "settle_steps": n_settle, "settle_min_ms": 40},
         "op_ms": {k: round(v, 4) for k, v in op_ms.items()},
