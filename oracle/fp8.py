@@ -21,17 +21,6 @@ ties to the even code, and maps magnitudes beyond 448 to 448 (saturating; the
 sign of a zero result is kept).  The value the
 attention sees is decode(code) * s_h.
 
-The query on fp8 matrix cores (an opt-in mode of the e4m3 cache, a further
-reading for the arithmetic, not the storage): the score products Q.K^T run
-with both operands in e4m3, so each query vector (one block row, one query
-head) is rounded to e4m3 as well.  It gets its own power-of-two scale 2^e, e the smallest integer
-with max_d |q_d| <= 448 * 2^e (e = 0 for an all-zero vector), so its largest
-element lands in (224, 448] and the division by the scale is exact:
-  qcode_d = round_e4m3(q_d / 2^e),   q seen by the attention = decode(qcode) * 2^e,
-with the same rounding as the cache.  A query whose elements are already
-e4m3 values times 2^e is unchanged.  The products of the values stay bf16
-products (P in bf16, V decoded exactly), as for the bf16 cache.
-
 Which K/V are quantised: every key and value the attention reads, the cached
 ones and the block's own rows alike.  Greedy decoding with such a cache writes a
 token's K/V and reads them back from the cache, so the verify pass must see the
@@ -39,9 +28,7 @@ block's keys exactly as the cache will hold them for its tokens to equal greedy
 decoding's [gist §2.3 step 3; HN #21, identical output distribution].  The
 commit then copies the quantised rows unchanged.
 
-Pinned by (tests/test_oracle_fp8.py): the query scale's defining inequalities
-by brute force (boundary, zero and subnormal rows among them) and its codes
-against PyTorch's float8_e4m3fn rounding; the closed-form values of the format's
+Pinned by (tests/test_oracle_fp8.py): the closed-form values of the format's
 landmark codes; PyTorch's float8_e4m3fn decoding of all 256 codes and its
 rounding of in-range values (a library routine); exact round trips of every
 finite code; the ties-to-even rule at every midpoint between neighbouring
@@ -117,46 +104,17 @@ def _along(s: np.ndarray, ndim: int, axis: int) -> np.ndarray:
     return s.reshape(shape)
 
 
-def query_exponents(q_bits) -> np.ndarray:
-    """bf16 queries [..., D] -> int64 e [...] per vector: the smallest integer
-    with max|q| <= 448 * 2^e (0 for an all-zero vector).  With max|q| = f * 2^E,
-    f in [0.5, 1), and 448 = 0.875 * 2^9, that is E - 9, or E - 8 when f > 0.875."""
-    q = from_bf16(q_bits)
-    if not np.all(np.isfinite(q)):
-        raise ValueError("query_exponents: the query must be finite")
-    amax = np.max(np.abs(q), axis=-1)
-    f, E = np.frexp(amax)
-    e = E.astype(np.int64) - 9 + (f > 0.875)
-    return np.where(amax == 0, 0, e)
-
-
-def quantize_query(q_bits) -> tuple[np.ndarray, np.ndarray]:
-    """bf16 queries [..., D] -> (e4m3 codes [..., D], exponents e [...]): each
-    vector divided by its power-of-two scale 2^e (exact) and rounded."""
-    e = query_exponents(q_bits)
-    x = np.ldexp(from_bf16(q_bits), -e[..., None])
-    return e4m3_encode(x), e
-
-
-def dequantize_query(codes, e) -> np.ndarray:
-    """(codes, exponents) -> float64 queries decode(code) * 2^e."""
-    return np.ldexp(e4m3_decode(codes), np.asarray(e)[..., None])
-
-
 def block_attention_fp8(q_bits, k_blk, v_blk, k_pages, v_pages, k_scale, v_scale,
                         block_table, seq_lens, mode: str, scale: float | None = None,
-                        page_size: int = 16, fp8_query: bool = False) -> np.ndarray:
+                        page_size: int = 16) -> np.ndarray:
     """Attention [B, K, Hq, D] (fp64) over an e4m3 cache.
 
     q_bits: bf16 [B,K,Hq,D]; k_blk, v_blk: e4m3 codes [B,K,Hkv,D] (the block's
     own rows, quantised like the cache); k_pages, v_pages: e4m3 codes
     [num_pages,Hkv,page_size,D]; k_scale, v_scale: fp32 [Hkv].  The keys and
     values are dequantised and the attention is the bf16 cache's
-    (oracle.attention.block_attention) on those values; with fp8_query the
-    queries are first rounded to e4m3 with their power-of-two scales
-    (quantize_query)."""
-    q = dequantize_query(*quantize_query(q_bits)) if fp8_query else from_bf16(q_bits)
-    return block_attention(q,
+    (oracle.attention.block_attention) on those values."""
+    return block_attention(from_bf16(q_bits),
                            dequantize_kv(k_blk, k_scale, head_axis=2),
                            dequantize_kv(v_blk, v_scale, head_axis=2),
                            dequantize_kv(k_pages, k_scale, head_axis=1),
