@@ -1,6 +1,7 @@
 // Host-side argument checking and launch planning (see check.h).
 #include "check.h"
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdio>
@@ -285,6 +286,9 @@ bool plan_sample(int stat_rows, int B, int V, SamplePlan* p) {
   p->ngroups = int(ceil_div(p->nchunks, kSampleGroup));
   p->rchunk = kResidualChunk;
   p->rchunks = B > 0 ? int(ceil_div(V, kResidualChunk)) : 0;
+  // every workgroup of the acceptance launch repeats the sequence's test, so
+  // the chunks are spread over at most one workgroup per CU
+  p->rcpw = int(std::max<int64_t>(1, ceil_div(int64_t(B) * p->rchunks, kResidualWorkgroups)));
   const int64_t cells = rows1 * p->nchunks, gcells = rows1 * p->ngroups;
   p->cm_off = 0;
   p->cs_off = p->cm_off + size_t(round_up(cells * 4, 256));

@@ -104,6 +104,7 @@ int check_commit(const orthrus_kv* kv, int layers, int64_t pool_layer_stride, co
 // per-sequence acceptance state and the residual chunk sums.
 constexpr int kSampleSeqBytes = 32;
 constexpr int kResidualChunk = 1024;   // entries per residual chunk
+constexpr int kResidualWorkgroups = 256;   // residual workgroups per call at most (one per CU)
 // Statistics chunks: one wavefront each, 16 entries per lane (1024), or 32
 // per lane (2048) when the 1024-entry chunks would need more wavefronts than
 // the GPU holds at once; four consecutive chunks of a row form a group.
@@ -118,6 +119,7 @@ struct SamplePlan {
   int B = 0, V = 0, chunk = 0, nchunks = 0;
   int ngroups = 0;               // groups of kSampleGroup chunks per row
   int rchunk = 0, rchunks = 0;   // residual chunks (consensus only)
+  int rcpw = 0;                  // residual chunks per workgroup of the acceptance launch
   size_t cm_off = 0, cs_off = 0, cw_off = 0, gm_off = 0, gs_off = 0, seq_off = 0, rs_off = 0, ws_bytes = 0;
 };
 

@@ -25,7 +25,9 @@
 // finds its chunk from the chunk weights and then its entry inside that
 // chunk (4 or 8 per thread), each time from a fixed-order prefix sum over
 // contiguous per-thread shares.  The residual of a rejected row has its own
-// chunk sums.
+// chunk sums, taken in the acceptance test's launch: each workgroup of that
+// launch repeats the sequence's test (the same arithmetic, so the same
+// outcome everywhere) and then sums its share of the rejected row.
 // (Handing the chunk results to the row's last workgroup within one launch
 // was measured slower: a device-scope fence per workgroup, or device-scope
 // atomics for the hand-over, cost more than the second launch.)
@@ -96,7 +98,8 @@ struct DecideArgs {
   int32_t* n_emit;
   int32_t* next_anchor;
   SeqState* seq;       // [B]
-  int B, K, V, ngroups;
+  double* rs;          // [B][rchunks] residual chunk sums
+  int B, K, V, ngroups, rchunk, rchunks, rcpw;
   double tscale;
 };
 
@@ -460,19 +463,25 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a) {
   if (threadIdx.x == 0) a.out[row] = tok;
 }
 
-// One workgroup per sequence: the maximum and normaliser of each of its 2K
-// statistics rows from their group statistics (a team of G threads per row,
-// groups strided over the team, then a butterfly within it), then
-// wavefront 0, lane i = block
-// row i, runs the acceptance test of every row and finds the first
-// rejection.
+// Acceptance test and residual chunk sums, one launch.  Workgroup (x, b)
+// first recomputes what every workgroup of sequence b needs: the maximum and
+// normaliser of each of its 2K statistics rows from their group statistics
+// (a team of G threads per row, groups strided over the team, then a
+// butterfly within it), then wavefront 0, lane i = block row i, runs the
+// acceptance test of every row and finds the first rejection j (workgroup 0
+// writes the sequence's outputs and state).  Then, if a row was rejected,
+// the workgroup sums the residual max(0, p - q) of row j over its rcpw
+// chunks of rchunk entries.  The test's arithmetic is the same in every
+// workgroup, so all of them see the same j.
 constexpr int kDecideThreads = 1024;
 
-__global__ __launch_bounds__(kDecideThreads) void sample_decide_kernel(DecideArgs a) {
+__global__ __launch_bounds__(kDecideThreads) void accept_residual_kernel(DecideArgs a) {
   __shared__ double tab[64];
   __shared__ RowNorm rn_s[2 * ORTHRUS_MAX_BLOCK];
+  __shared__ SeqState st_s;
+  __shared__ double redd[kDecideThreads / kThreads][4];
   constexpr int kReg = 16;                         // chunks per thread per batch of loads
-  const int b = blockIdx.x;
+  const int b = blockIdx.y;
   const int BK = a.B * a.K, R = 2 * a.K;
   // the table first, so that waiting for it does not wait for the loads below
   const double tab_v = threadIdx.x < 64 ? kExp2Frac[threadIdx.x] : 0.0;
@@ -544,50 +553,61 @@ __global__ __launch_bounds__(kDecideThreads) void sample_decide_kernel(DecideArg
     if (gl == 0) rn_s[r] = RowNorm{zs, m, 0};
   }
   __syncthreads();
-  if (threadIdx.x >= 64) return;
-  bool reject = false;
-  RowNorm nd{0.0, 0.f, 0}, na{0.0, 0.f, 0};
-  if (lane_row) {
-    nd = rn_s[i];
-    na = rn_s[a.K + i];
-    double p = 0.0, q = 0.0;                       // a token outside the vocabulary has p = q = 0
-    if (in_vocab) {
-      p = wexp(zta, na.M, a.tscale, tab) / na.Z;
-      q = wexp(ztd, nd.M, a.tscale, tab) / nd.Z;
+  if (threadIdx.x < 64) {
+    bool reject = false;
+    RowNorm nd{0.0, 0.f, 0}, na{0.0, 0.f, 0};
+    if (lane_row) {
+      nd = rn_s[i];
+      na = rn_s[a.K + i];
+      double p = 0.0, q = 0.0;                     // a token outside the vocabulary has p = q = 0
+      if (in_vocab) {
+        p = wexp(zta, na.M, a.tscale, tab) / na.Z;
+        q = wexp(ztd, nd.M, a.tscale, tab) / nd.Z;
+      }
+      reject = !(double(uacc) * q < p);
     }
-    reject = !(double(uacc) * q < p);
-  }
-  const unsigned long long bad = __ballot(reject);
-  const int j = bad ? (__ffsll(static_cast<long long>(bad)) - 1) : a.K;
-  if (lane_row) a.tokens[size_t(b) * a.K + i] = i < j ? t : -1;
-  if (i == 0) {
-    a.n_acc[b] = j;
-    a.n_emit[b] = j < a.K ? j + 1 : a.K;
-    if (j == a.K) {
-      a.next_anchor[b] = a.draft[size_t(b) * a.K + a.K - 1];
-      a.seq[b] = SeqState{0.0, 0.0, 0.f, 0.f, a.K, 0};
+    const unsigned long long bad = __ballot(reject);
+    const int j = bad ? (__ffsll(static_cast<long long>(bad)) - 1) : a.K;
+    const SeqState none{0.0, 0.0, 0.f, 0.f, a.K, 0};
+    if (blockIdx.x == 0) {                         // the sequence's outputs, once
+      if (lane_row) a.tokens[size_t(b) * a.K + i] = i < j ? t : -1;
+      if (i == 0) {
+        a.n_acc[b] = j;
+        a.n_emit[b] = j < a.K ? j + 1 : a.K;
+        if (j == a.K) {
+          a.next_anchor[b] = a.draft[size_t(b) * a.K + a.K - 1];
+          a.seq[b] = none;
+        }
+      }
+      if (i == j) a.seq[b] = SeqState{na.Z, nd.Z, na.M, nd.M, j, 0};
     }
+    if (i == 0 && j == a.K) st_s = none;
+    if (i == j) st_s = SeqState{na.Z, nd.Z, na.M, nd.M, j, 0};
   }
-  if (i == j) a.seq[b] = SeqState{na.Z, nd.Z, na.M, nd.M, j, 0};
-}
-
-// Sums of the residual max(0, p - q) of each sequence's rejected row over
-// chunks of rchunk entries.
-__global__ __launch_bounds__(kThreads) void residual_stats_kernel(ResidualArgs a) {
-  __shared__ double redd[4];
-  __shared__ double tab[64];
-  const int b = blockIdx.y, c = blockIdx.x;
-  const SeqState st = a.seq[b];
-  if (st.j >= a.K) return;                         // uniform: nothing rejected
-  load_exp_table(tab);
   __syncthreads();
+  // Residual chunk sums of the rejected row: the workgroup's rcpw chunks,
+  // four at a time, each by one group of 256 threads (4 entries per thread
+  // in order, then the group's four wavefront sums in order).
+  const SeqState st = st_s;
+  if (st.j >= a.K) return;                         // uniform: nothing rejected
   const size_t row = size_t(b) * a.K + st.j;
-  const ResidualEntry r{a.za + row * a.V, a.zd + row * a.V, st.Ma, st.Md, st.Za, st.Zd, a.tscale, tab};
-  const int v0 = c * a.rchunk, v1 = min(v0 + a.rchunk, a.V);
-  double s = 0.0;
-  for (int v = v0 + threadIdx.x; v < v1; v += kThreads) s += r.weight(r.load(v));
-  s = block_sum(s, redd);
-  if (threadIdx.x == 0) a.rs[size_t(b) * a.rchunks + c] = s;
+  const ResidualEntry res{a.za + row * a.V, a.zd + row * a.V, st.Ma, st.Md, st.Za, st.Zd, a.tscale, tab};
+  const int grp = threadIdx.x / kThreads, gt = threadIdx.x % kThreads;
+  const int c0 = blockIdx.x * a.rcpw;
+  const int c1 = min(c0 + a.rcpw, a.rchunks);
+  for (int cb = c0; cb < c1; cb += kDecideThreads / kThreads) {      // uniform
+    const int c = cb + grp;
+    double sum = 0.0;
+    if (c < c1) {
+      const int v0 = c * a.rchunk, v1 = min(v0 + a.rchunk, a.V);
+      for (int v = v0 + gt; v < v1; v += kThreads) sum += res.weight(res.load(v));
+    }
+    sum = wave_sum(sum);
+    if ((gt & 63) == 0) redd[grp][gt >> 6] = sum;
+    __syncthreads();
+    if (gt == 0 && c < c1) a.rs[size_t(b) * a.rchunks + c] = ((redd[grp][0] + redd[grp][1]) + redd[grp][2]) + redd[grp][3];
+    __syncthreads();                               // redd is free for the next four chunks
+  }
 }
 
 // One workgroup per sequence: the emitted token at the rejected row, a draw
@@ -690,13 +710,12 @@ hipError_t launch_accept_sampled(const SamplePlan& p, const float* logits_d, con
                                            p.nchunks, p.ngroups, tscale}, stream);
   if (e != hipSuccess) return e;
   const DecideArgs d{logits_d, logits_a, draft, u_acc, w.gm, w.gs, tokens, n_acc, n_emit, next_anchor, w.seq,
-                     B, K, p.V, p.ngroups, tscale};
-  e = launch_kernel(&sample_decide_kernel, dim3(B), dim3(kDecideThreads), stream, d);
+                     w.rs, B, K, p.V, p.ngroups, p.rchunk, p.rchunks, p.rcpw, tscale};
+  e = launch_kernel(&accept_residual_kernel, dim3(unsigned((p.rchunks + p.rcpw - 1) / p.rcpw), unsigned(B)),
+                    dim3(kDecideThreads), stream, d);
   if (e != hipSuccess) return e;
   const ResidualArgs r{logits_d, logits_a, u_res, w.cm, w.cs, w.seq, w.rs, tokens, next_anchor,
                        B, K, p.V, p.chunk, p.nchunks, p.rchunk, p.rchunks, tscale};
-  e = launch_kernel(&residual_stats_kernel, dim3(p.rchunks, B), dim3(kThreads), stream, r);
-  if (e != hipSuccess) return e;
   return launch_kernel(&residual_draw_kernel, dim3(B), dim3(kThreads), stream, r);
 }
 

@@ -98,6 +98,12 @@ int main() {
   EXPECT(plan_sample(47, 0, 151936, &sp) && sp.chunk == 1024);
   EXPECT(plan_sample(48, 0, 151936, &sp) && sp.chunk == 2048 && sp.nchunks == 75 && sp.ngroups == 19);
   EXPECT(plan_sample(2 * 16 * 32, 16, 151936, &sp) && sp.nchunks == 75 && sp.rchunks == 149);
+  EXPECT(sp.rcpw == 10 && (sp.rchunks + sp.rcpw - 1) / sp.rcpw * 16 <= 256);   // one workgroup per CU at most
+  {
+    SamplePlan s1;
+    EXPECT(plan_sample(2 * 32, 1, 151936, &s1) && s1.rchunks == 149 && s1.rcpw == 1);
+    EXPECT(plan_sample(2 * 32, 0, 151936, &s1) && s1.rchunks == 0 && s1.rcpw == 1);
+  }
   EXPECT(sp.cs_off >= size_t(1024) * 75 * 4 && sp.gs_off >= sp.gm_off + size_t(1024) * 19 * 4);
   EXPECT(sp.rs_off + size_t(16) * sp.rchunks * 8 <= sp.ws_bytes);
   EXPECT(plan_sample(1, 0, 4200000, &sp) && sp.nchunks == 4102 && sp.ngroups == 1026);
