@@ -139,6 +139,7 @@ def run_accept(lib, zd, za, d, T, u_acc, u_res):
     (5, 2, 64, 2048, 0.5, 0.98),
     (6, 1, 64, 151936, 0.9, 0.9),      # K = 64 at the 8B vocabulary: 149 chunks per row, 8 threads per row
     (7, 8, 8, 151936, 1.0, 0.6),       # 5 residual chunks per workgroup: two rounds of the 4 chunk groups
+    (8, 2, 64, 151936, 0.8, 0.9),      # K = 64 with 2 residual chunks per workgroup
 ])
 def test_accept_sampled_matches_oracle(lib, seed, B, K, V, T, agree):
     from oracle.sampling import speculative_accept
